@@ -1,0 +1,145 @@
+"""The oracle: a plain fp64 CPU reference for the W4A16 GEMM and its packing rule.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check in __graft_entry__ and the
+bench's CPU-baseline leg may import this package. It shares no code with the HIP
+library and never imports it.
+
+The C source (w4a16_oracle.c) states the operation and the pages it follows; this
+module builds it with gcc and wraps it with ctypes over numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "w4a16_oracle.c")
+BUILD_DIR = os.path.join(_HERE, "_build")
+LIB_PATH = os.path.join(BUILD_DIR, "liboracle_w4a16.so")
+
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(out_path: str = LIB_PATH, source: str = SOURCE, extra_cflags: Sequence[str] = ()) -> str:
+    """Compile the oracle with gcc into a shared library and return its path."""
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    tmp = out_path + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *CFLAGS, *extra_cflags, source, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class Oracle:
+    """ctypes wrapper around one build of the oracle library."""
+
+    def __init__(self, lib_path: str = LIB_PATH):
+        if not os.path.exists(lib_path):
+            build(lib_path)
+        self.path = lib_path
+        lib = ctypes.CDLL(lib_path)
+        i64 = ctypes.c_int64
+        vp = ctypes.c_void_p
+        lib.oracle_w4a16_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, ctypes.c_int]
+        lib.oracle_w4a16_gemm.restype = ctypes.c_int
+        lib.oracle_w4_pack.argtypes = [vp, vp, i64, i64]
+        lib.oracle_w4_pack.restype = ctypes.c_int
+        lib.oracle_w4_unpack.argtypes = [vp, vp, i64, i64]
+        lib.oracle_w4_unpack.restype = ctypes.c_int
+        lib.oracle_decode_bf16_array.argtypes = [vp, vp, i64]
+        lib.oracle_decode_f16_array.argtypes = [vp, vp, i64]
+        lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.oracle_f16_to_f64.restype = ctypes.c_double
+        self._lib = lib
+
+    # -- decoders -----------------------------------------------------------------
+    def bf16_to_f64(self, bits: np.ndarray) -> np.ndarray:
+        b = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(b.shape, dtype=np.float64)
+        self._lib.oracle_decode_bf16_array(_ptr(b), _ptr(out), b.size)
+        return out
+
+    def f16_to_f64(self, bits: np.ndarray) -> np.ndarray:
+        b = np.ascontiguousarray(bits, dtype=np.uint16)
+        out = np.empty(b.shape, dtype=np.float64)
+        self._lib.oracle_decode_f16_array(_ptr(b), _ptr(out), b.size)
+        return out
+
+    # -- packing ------------------------------------------------------------------
+    def pack(self, q: np.ndarray) -> np.ndarray:
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        K, N = q.shape
+        out = np.empty((K // 8, N), dtype=np.uint32)
+        rc = self._lib.oracle_w4_pack(_ptr(q), _ptr(out), K, N)
+        if rc:
+            raise ValueError(f"oracle pack rejected shape {q.shape}")
+        return out
+
+    def unpack(self, Wq: np.ndarray) -> np.ndarray:
+        Wq = np.ascontiguousarray(Wq, dtype=np.uint32)
+        KB, N = Wq.shape
+        out = np.empty((KB * 8, N), dtype=np.uint8)
+        rc = self._lib.oracle_w4_unpack(_ptr(Wq), _ptr(out), KB * 8, N)
+        if rc:
+            raise ValueError(f"oracle unpack rejected shape {Wq.shape}")
+        return out
+
+    # -- the GEMM -----------------------------------------------------------------
+    def gemm(self, A: np.ndarray, Wq: np.ndarray, S: np.ndarray, Z: np.ndarray,
+             cols: Optional[np.ndarray] = None, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """Return (C, Cabs), both float64 [M, ncols]: C = A.W and Cabs = sum_k |A.W| terms.
+
+        A: uint16 bf16 bits [M,K]; Wq: uint32 [K/8,N]; S: uint16 fp16 bits [K/128,N];
+        Z: uint8 [K/128,N]; cols: optional int64 column indices.
+        """
+        A = np.ascontiguousarray(A, dtype=np.uint16)
+        Wq = np.ascontiguousarray(Wq, dtype=np.uint32)
+        S = np.ascontiguousarray(S, dtype=np.uint16)
+        Z = np.ascontiguousarray(Z, dtype=np.uint8)
+        M, K = A.shape
+        KB, N = Wq.shape
+        if KB * 8 != K or S.shape != (K // 128, N) or Z.shape != (K // 128, N):
+            raise ValueError("inconsistent shapes")
+        if cols is not None:
+            cols = np.ascontiguousarray(cols, dtype=np.int64)
+            nc = cols.size
+        else:
+            nc = N
+        C = np.empty((M, nc), dtype=np.float64)
+        Cabs = np.empty((M, nc), dtype=np.float64)
+        rc = self._lib.oracle_w4a16_gemm(_ptr(A), _ptr(Wq), _ptr(S), _ptr(Z), M, K, N,
+                                         _ptr(cols), nc, _ptr(C), _ptr(Cabs), int(threads))
+        if rc:
+            raise ValueError(f"oracle rejected the shape M={M} K={K} N={N} (rc={rc})")
+        return C, Cabs
+
+
+_default: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    """The shared oracle instance (built on first use if the library is missing)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def within_tolerance(C_test: np.ndarray, C_ref: np.ndarray, Cabs: np.ndarray,
+                     rel: float = 1e-4, abs_: float = 1e-6) -> np.ndarray:
+    """Element-wise acceptance: |C_test - C_ref| <= rel * sum_k|A W| + abs_ (in float64)."""
+    err = np.abs(np.asarray(C_test, dtype=np.float64) - C_ref)
+    return err <= rel * Cabs + abs_

@@ -1,0 +1,334 @@
+"""Pins for the oracle: checks that tie it to something other than itself.
+
+Each pin takes an `oracle.Oracle` and raises AssertionError when the oracle disagrees
+with what the mathematics or a worked example fixes. The pins are collected by
+test_oracle_pins.py (run against the real oracle) and by test_oracle_mutants.py (run
+against copies of the oracle with one plausible mistake planted, each of which must
+fail at least one pin).
+
+What pins what:
+  * decoders: every one of the 65536 fp16 and bf16 bit patterns against numpy's own
+    float16 and float32 conversions (hardware IEEE decoding, not the oracle's code);
+  * packing: hand-worked words (tests/golden/pack_words.txt), round trips both ways,
+    high-nibble masking;
+  * the GEMM: hand-computed closed forms (tests/golden/closed_forms.txt), the identity
+    case q=z+1, s=1 (row sums of A), the all-ones-A case (integer column sums of the
+    codes), one-hot A (row extraction), q=z and s=0 (exact zeros), exact rational brute
+    force with Python fractions on tiny shapes, a BLAS float64 matmul of an explicitly
+    dequantized W at a mid size, power-of-two scaling, column sampling and thread-count
+    invariance.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------------------
+# independent helpers (numpy / Python only; they do not call the oracle)
+def np_bf16_to_f64(bits):
+    with np.errstate(invalid="ignore"):
+        return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def np_f16_to_f64(bits):
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def np_unpack(Wq):
+    Wq = np.asarray(Wq, np.uint32)
+    KB, N = Wq.shape
+    shifts = (4 * np.arange(8, dtype=np.uint32))[None, :, None]
+    return ((Wq[:, None, :] >> shifts) & 0xF).reshape(KB * 8, N).astype(np.uint8)
+
+
+def np_pack(q):
+    q = np.asarray(q, np.uint8) & 0xF
+    K, N = q.shape
+    q8 = q.reshape(K // 8, 8, N).astype(np.uint32)
+    w = np.zeros((K // 8, N), np.uint32)
+    for j in range(8):
+        w |= q8[:, j, :] << np.uint32(4 * j)
+    return w
+
+
+def bf16_bits(values):
+    """Exact bf16 encodings of values that are exactly representable."""
+    v = np.asarray(values, np.float32)
+    bits = v.view(np.uint32)
+    assert np.all((bits & 0xFFFF) == 0), "value not exactly representable in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def f16_bits(values):
+    v = np.asarray(values, np.float64)
+    h = v.astype(np.float16)
+    assert np.all(h.astype(np.float64) == v), "value not exactly representable in fp16"
+    return h.view(np.uint16)
+
+
+# ---------------------------------------------------------------------------------------
+def pin_f16_decoder_exhaustive(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.f16_to_f64(bits)
+    ref = np_f16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # the sign of zero is kept
+    assert math.copysign(1.0, got[0x8000]) == -1.0
+
+
+def pin_bf16_decoder_exhaustive(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.bf16_to_f64(bits)
+    ref = np_bf16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def _golden_pack_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "pack_words.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            rows.append(([int(p) for p in parts[:8]], int(parts[8], 16)))
+    return rows
+
+
+def pin_pack_golden(o):
+    rows = _golden_pack_rows()
+    assert len(rows) >= 8
+    q = np.array([r[0] for r in rows], dtype=np.uint8).T.copy()  # [8, n]
+    words = o.pack(q)
+    assert words.shape == (1, len(rows))
+    for i, (_, w) in enumerate(rows):
+        assert int(words[0, i]) == w, f"golden row {i}: {int(words[0, i]):#010x} != {w:#010x}"
+    # unpack returns the low nibbles of the golden inputs
+    assert np.array_equal(o.unpack(words), q & 0xF)
+
+
+def pin_pack_roundtrip(o):
+    r = np.random.default_rng(7)
+    q = r.integers(0, 16, size=(64, 37), dtype=np.uint8)
+    w = o.pack(q)
+    assert np.array_equal(o.unpack(w), q)
+    assert np.array_equal(w, np_pack(q))
+    words = r.integers(0, 1 << 32, size=(9, 13), dtype=np.uint32)
+    assert np.array_equal(o.pack(o.unpack(words)), words)
+    assert np.array_equal(o.unpack(words), np_unpack(words))
+
+
+def pin_pack_high_nibble(o):
+    r = np.random.default_rng(8)
+    q = r.integers(0, 256, size=(32, 19), dtype=np.uint8)
+    assert np.array_equal(o.pack(q), o.pack(q & 0xF))
+    assert np.array_equal(o.unpack(o.pack(q)), q & 0xF)
+
+
+def _closed_form_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "closed_forms.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = [p.strip() for p in line.split("|")]
+            K = int(parts[0])
+            groups = [tuple(float(v) for v in p.split()) for p in parts[1:-1]]
+            rows.append((K, groups, float(parts[-1])))
+    return rows
+
+
+def pin_closed_forms(o):
+    rows = _closed_form_rows()
+    assert len(rows) >= 4
+    for K, groups, expect in rows:
+        G = K // 128
+        assert len(groups) == G
+        N = 3
+        A = np.zeros((2, K), np.float32)
+        q = np.zeros((K, N), np.uint8)
+        S = np.zeros((G, N), np.float64)
+        Z = np.zeros((G, N), np.uint8)
+        for g, (a, qq, zz, ss) in enumerate(groups):
+            A[:, g * 128:(g + 1) * 128] = a
+            q[g * 128:(g + 1) * 128, :] = int(qq)
+            Z[g, :] = int(zz)
+            S[g, :] = ss
+        C, Cabs = o.gemm(bf16_bits(A), np_pack(q), f16_bits(S), Z)
+        assert np.all(C == expect), (K, groups, C, expect)
+        assert np.all(Cabs >= np.abs(C))
+
+
+def pin_identity_rowsum(o):
+    # q = z + 1 and s = 1 make W all ones, so C[m, n] is the row sum of A for every n.
+    M, K, N = 3, 384, 11
+    r = np.random.default_rng(11)
+    A = synth.f32_to_bf16_bits(r.standard_normal((M, K), dtype=np.float32))
+    Z = r.integers(0, 15, size=(K // 128, N), dtype=np.uint8)
+    q = np.repeat(Z + 1, 128, axis=0).astype(np.uint8)
+    S = f16_bits(np.ones((K // 128, N)))
+    C, _ = o.gemm(A, np_pack(q), S, Z)
+    a = np_bf16_to_f64(A)
+    for m in range(M):
+        rs = math.fsum(a[m])
+        assert np.all(np.abs(C[m] - rs) <= K * 2.0 ** -53 * np.sum(np.abs(a[m])))
+
+
+def pin_all_ones(o):
+    # A = 1: C[m, n] = sum_g s[g,n] * (sum_{k in g} q[k,n] - 128 z[g,n]), integer inner sums.
+    M, K, N = 2, 512, 9
+    r = np.random.default_rng(12)
+    q = r.integers(0, 16, size=(K, N), dtype=np.uint8)
+    Z = r.integers(0, 16, size=(K // 128, N), dtype=np.uint8)
+    S = synth.draw_scales(r, K // 128, N)
+    A = bf16_bits(np.ones((M, K), np.float32))
+    C, Cabs = o.gemm(A, np_pack(q), S, Z)
+    s = np_f16_to_f64(S)
+    for n in range(N):
+        exact = Fraction(0)
+        for g in range(K // 128):
+            isum = int(q[g * 128:(g + 1) * 128, n].astype(np.int64).sum()) - 128 * int(Z[g, n])
+            exact += Fraction(s[g, n]) * isum
+        for m in range(M):
+            assert abs(Fraction(C[m, n]) - exact) <= Fraction(K) * Fraction(2) ** -53 * Fraction(Cabs[m, n])
+
+
+def pin_one_hot(o):
+    # A = a0 * e_{m0,k0}: row m0 of C is a0 * (q[k0,:] - z[g0,:]) * s[g0,:]; other rows are 0.
+    M, K, N = 4, 384, 21
+    x = synth.generate_custom(M, K, N, seed=13)
+    q = np_unpack(x.Wq)
+    s = np_f16_to_f64(x.S)
+    for (m0, k0, a0) in ((0, 0, 1.0), (1, 7, -2.5), (3, 130, 0.375), (2, 255, 96.0), (1, 383, -0.0078125)):
+        A = np.zeros((M, K), np.float32)
+        A[m0, k0] = a0
+        C, _ = o.gemm(bf16_bits(A), x.Wq, x.S, x.Z)
+        g0 = k0 // 128
+        expect = a0 * (q[k0].astype(np.float64) - (x.Z[g0] & 0xF)) * s[g0]
+        assert np.array_equal(C[m0], expect), (m0, k0)
+        others = [m for m in range(M) if m != m0]
+        assert np.all(C[others] == 0.0)
+
+
+def pin_zero_cases(o):
+    M, K, N = 3, 256, 17
+    x = synth.generate_custom(M, K, N, seed=14)
+    # q = z everywhere -> exactly zero
+    q = np.repeat(x.Z, 128, axis=0).astype(np.uint8)
+    C, Cabs = o.gemm(x.A, np_pack(q), x.S, x.Z)
+    assert np.all(C == 0.0) and np.all(Cabs == 0.0)
+    # s = 0 -> exactly zero
+    C, _ = o.gemm(x.A, x.Wq, np.zeros_like(x.S), x.Z)
+    assert np.all(C == 0.0)
+
+
+def pin_zero_high_nibble(o):
+    M, K, N = 2, 256, 13
+    x = synth.generate_custom(M, K, N, seed=15)
+    r = np.random.default_rng(15)
+    Zg = (x.Z | (r.integers(1, 16, size=x.Z.shape, dtype=np.uint8) << 4)).astype(np.uint8)
+    C1, _ = o.gemm(x.A, x.Wq, x.S, x.Z)
+    C2, _ = o.gemm(x.A, x.Wq, x.S, Zg)
+    assert np.array_equal(C1, C2)
+
+
+def _exact_gemm(A, Wq, S, Z):
+    a = np_bf16_to_f64(A)
+    q = np_unpack(Wq).astype(np.int64)
+    s = np_f16_to_f64(S)
+    z = (np.asarray(Z) & 0xF).astype(np.int64)
+    M, K = a.shape
+    N = q.shape[1]
+    C = [[Fraction(0)] * N for _ in range(M)]
+    B = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        for k in range(K):
+            g = k // 128
+            w = Fraction(s[g, n]) * int(q[k, n] - z[g, n])
+            for m in range(M):
+                t = Fraction(a[m, k]) * w
+                C[m][n] += t
+                B[m][n] += abs(t)
+    return C, B
+
+
+def pin_brute_force(o):
+    for (M, K, N, seed) in ((1, 128, 3, 1), (3, 256, 5, 2), (2, 128, 4, 3)):
+        x = synth.generate_custom(M, K, N, seed=100 + seed)
+        Zg = (x.Z | np.uint8(0xA0)).astype(np.uint8)  # high nibbles must not matter
+        C, Cabs = o.gemm(x.A, x.Wq, x.S, Zg)
+        Ce, Be = _exact_gemm(x.A, x.Wq, x.S, x.Z)
+        bound_scale = Fraction(K) * Fraction(2) ** -53
+        for m in range(M):
+            for n in range(N):
+                assert abs(Fraction(C[m, n]) - Ce[m][n]) <= bound_scale * Be[m][n], (M, K, N, m, n)
+                assert abs(Fraction(Cabs[m, n]) - Be[m][n]) <= bound_scale * Be[m][n], (M, K, N, m, n)
+
+
+def pin_numpy_matmul(o):
+    # mid size: a BLAS float64 matmul of an explicitly dequantized W (numpy decoding)
+    M, K, N = 5, 1536, 1536
+    x = synth.generate(synth.WORKLOADS["single-m5-k1536-n1536"].gemms[0])
+    Wq = np_pack(x.q)
+    C, Cabs = o.gemm(x.A, Wq, x.S, x.Z)
+    g = np.arange(K) // 128
+    W = (x.q.astype(np.float64) - (x.Z[g] & 0xF)) * np_f16_to_f64(x.S)[g]
+    Cn = np_bf16_to_f64(x.A) @ W
+    assert np.all(np.abs(Cn - C) <= 1e-12 * Cabs)
+    absn = np.abs(np_bf16_to_f64(x.A)) @ np.abs(W)
+    assert np.all(np.abs(absn - Cabs) <= 1e-12 * Cabs)
+
+
+def pin_power_of_two_scaling(o):
+    M, K, N = 3, 256, 7
+    x = synth.generate_custom(M, K, N, seed=16)
+    C, _ = o.gemm(x.A, x.Wq, x.S, x.Z)
+    A2 = bf16_bits(np_bf16_to_f64(x.A).astype(np.float32) * np.float32(4.0))
+    C2, _ = o.gemm(A2, x.Wq, x.S, x.Z)
+    assert np.array_equal(C2, 4.0 * C)
+    S2 = f16_bits(np_f16_to_f64(x.S) * 0.5)
+    C3, _ = o.gemm(x.A, x.Wq, S2, x.Z)
+    assert np.array_equal(C3, 0.5 * C)
+
+
+def pin_column_sampling_and_threads(o):
+    M, K, N = 4, 512, 97
+    x = synth.generate_custom(M, K, N, seed=17)
+    C, Cabs = o.gemm(x.A, x.Wq, x.S, x.Z)
+    C1, _ = o.gemm(x.A, x.Wq, x.S, x.Z, threads=1)
+    assert np.array_equal(C, C1)
+    cols = np.array([96, 0, 41, 41, 7], np.int64)
+    Cs, Cabss = o.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+    assert np.array_equal(Cs, C[:, cols]) and np.array_equal(Cabss, Cabs[:, cols])
+
+
+ALL_PINS = [
+    pin_f16_decoder_exhaustive,
+    pin_bf16_decoder_exhaustive,
+    pin_pack_golden,
+    pin_pack_roundtrip,
+    pin_pack_high_nibble,
+    pin_closed_forms,
+    pin_identity_rowsum,
+    pin_all_ones,
+    pin_one_hot,
+    pin_zero_cases,
+    pin_zero_high_nibble,
+    pin_brute_force,
+    pin_numpy_matmul,
+    pin_power_of_two_scaling,
+    pin_column_sampling_and_threads,
+]

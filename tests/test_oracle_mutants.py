@@ -1,0 +1,57 @@
+"""Each plausible mistake planted in a copy of the oracle must fail at least one pin.
+
+The mistakes are planted in the oracle's C source (on the CPU, in a temporary build); the
+HIP library is never involved. A mutation whose anchor text is missing fails loudly, so the
+list cannot silently go stale when the oracle is edited.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "nibble_order_reversed": ("(w >> (4 * (k % 8)))", "(w >> (4 * (7 - k % 8)))"),
+    "wrong_group_index": ("int64_t g = k / ORACLE_GROUP;",
+                          "int64_t g = (k / ORACLE_GROUP + 1) % (K / ORACLE_GROUP);"),
+    "zero_not_subtracted": ("int d = oracle_code(Wq, N, k, n) - zero;",
+                            "int d = oracle_code(Wq, N, k, n) - 0 * zero;"),
+    "zero_sign_flipped": ("int d = oracle_code(Wq, N, k, n) - zero;",
+                          "int d = zero - oracle_code(Wq, N, k, n);"),
+    "zero_high_nibble_kept": ("int zero = Z[g * N + n] & 0xF;", "int zero = Z[g * N + n];"),
+    "scale_from_next_column": ("oracle_f16_to_f64(S[g * N + n])",
+                               "oracle_f16_to_f64(S[g * N + (n + 1) % N])"),
+    "codes_mirrored_columns": ("uint32_t w = Wq[(k / 8) * N + n];",
+                               "uint32_t w = Wq[(k / 8) * N + (N - 1 - n)];"),
+    "activations_mirrored_k": ("oracle_bf16_to_f64(A[m * K + k])",
+                               "oracle_bf16_to_f64(A[m * K + (K - 1 - k)])"),
+    "f16_exponent_bias": ("e - 15 - 10", "e - 16 - 10"),
+    "f16_subnormal_scale": ("ldexp((double)f, -24)", "ldexp((double)f, -25)"),
+    "bf16_implicit_bit": ("(double)(128 + f)", "(double)(127 + f)"),
+    "bf16_subnormal_scale": ("ldexp((double)f, -126 - 7)", "ldexp((double)f, -126 - 6)"),
+    "pack_shift_reversed": ("<< (4 * j);", "<< (4 * (7 - j));"),
+    "pack_mask_dropped": ("(uint32_t)(q[(8 * kb + j) * N + n] & 0xF)", "(uint32_t)(q[(8 * kb + j) * N + n])"),
+    "abs_sum_signed": ("abs_acc[m] += fabs(t);", "abs_acc[m] += t;"),
+    "accumulate_in_float": ("acc[m] += t;", "acc[m] = (float)(acc[m] + t);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"anchor for mutant {name} not found in the oracle source"
+    mutated = src.replace(old, new)
+    path = tmp_path / f"{name}.c"
+    path.write_text(mutated)
+    lib = oracle.build(str(tmp_path / f"lib_{name}.so"), source=str(path))
+    o = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
