@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Throughput of the W4A16 GEMM on one MI355X, on synthetic model-shaped workloads.
+
+One step = every linear layer of one forward of the named workload (default: the
+Qwen2.5-7B-shaped verify pass at M = gamma + 1 = 5: 28 layers x {qkv, o, gate_up, down} =
+112 GEMMs), with all inputs resident in HBM before timing starts.  The step is captured
+once into a HIP graph and replayed; W untimed replays, then K timed replays bracketed by
+synchronization, timed with HIP events on the launch stream.
+
+Printed (one JSON line): effective weight GB/s (weight bytes = 4-bit codes + fp16 scales
++ u8 zeros per 128, i.e. 0.5234375 B per weight, divided by the step time), the fraction
+of the 8 TB/s HBM peak, the dominant kernel's roofline figures (per-launch durations from
+HIP events in a separate pass) and the oracle timed on the host cores on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+METRIC = "W4A16 verify-GEMM effective weight GB/s and % of HBM roofline at M=gamma+1"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(ROOT, "int4_weight_only_gemm_amd", "csrc", "w4a16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w4a16_small_m_kernel.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen2.5-7b-verify-m5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--roofline-steps", type=int, default=3)
+    ap.add_argument("--eager-steps", type=int, default=0,
+                    help="only run this many eager steps (for a profiler) and print nothing else")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB 5 times (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the GEMM would shard by output columns; see DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import int4_weight_only_gemm_amd as w4
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: 5 copies of {args.copy_probe_mib} MiB")
+        return
+
+    wl = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    gemms = []  # (spec, device tensors, out)
+    host_sample = []
+    for i, spec in enumerate(wl.gemms):
+        x = synth.generate(spec)
+        d = {
+            "A": torch.from_numpy(x.A.view(np.int16)).to(dev).view(torch.bfloat16),
+            "S": torch.from_numpy(x.S.view(np.int16)).to(dev).view(torch.float16),
+            "Z": torch.from_numpy(x.Z).to(dev),
+        }
+        if x.Wq is not None:
+            d["Wq"] = torch.from_numpy(x.Wq.view(np.int32)).to(dev)
+        else:
+            d["Wq"] = w4.pack(torch.from_numpy(x.q).to(dev))
+        d["C"] = torch.empty((spec.M, spec.N), dtype=torch.float32, device=dev)
+        gemms.append((spec, d))
+        if i < 4:
+            host_sample.append((spec, x))
+    torch.cuda.synchronize()
+    log(f"{args.workload}: {len(gemms)} GEMMs, {wl.weight_bytes / 1e9:.3f} GB of weights, "
+        f"inputs ready in {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.Stream(device=dev)
+    handle = stream.cuda_stream
+    calls = [(d["A"].data_ptr(), d["Wq"].data_ptr(), d["S"].data_ptr(), d["Z"].data_ptr(), d["C"].data_ptr(),
+              spec.M, spec.K, spec.N) for spec, d in gemms]
+    lib = w4.lib()
+
+    def step():
+        for c in calls:
+            rc = lib.w4a16_gemm(*c, handle)
+            if rc:
+                raise w4.W4Error(rc, "w4a16_gemm")
+
+    # one eager step sizes the split-K workspace of this stream before capture
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+
+    if args.eager_steps:
+        with torch.cuda.stream(stream):
+            for i in range(args.eager_steps):
+                step()
+                torch.cuda.synchronize()
+                log(f"eager step {i + 1}/{args.eager_steps} done")
+        return
+
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize()
+
+    def run_step():
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            run_step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run_step()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed_ms = ev0.elapsed_time(ev1)
+    ms_per_step = elapsed_ms / args.steps
+    gbs = wl.weight_bytes / (ms_per_step * 1e-3) / 1e9
+    tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, {gbs:.1f} GB/s, {tflops:.2f} TFLOP/s")
+
+    # Roofline pass: per-launch HIP events on the launch stream. A GPU-side sleep first lets
+    # the host queue every launch, so each interval is the kernel's own execution.
+    n_launch = args.roofline_steps * len(calls)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
+    with torch.cuda.stream(stream):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(2e8))
+        i = 0
+        for _ in range(args.roofline_steps):
+            for c in calls:
+                evs[i][0].record(stream)
+                rc = lib.w4a16_gemm(*c, handle)
+                if rc:
+                    raise w4.W4Error(rc, "w4a16_gemm")
+                evs[i][1].record(stream)
+                i += 1
+    torch.cuda.synchronize()
+    durs = np.array([a.elapsed_time(b) for a, b in evs]).reshape(args.roofline_steps, len(calls))
+    bytes_per_launch = np.array([spec.weight_bytes for spec, _ in gemms], dtype=np.float64)
+    flops_per_launch = np.array([spec.flops for spec, _ in gemms], dtype=np.float64)
+    avg_dur_ms = float(durs.mean())
+    mfma_bound = max(spec.M for spec, _ in gemms) >= 64
+    if mfma_bound:  # batched verify: a dense contraction, priced against the fp16 MFMA peak
+        achieved = float(flops_per_launch.mean()) / (avg_dur_ms * 1e-3) / 1e12
+        peak, unit, bound = MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved = float(bytes_per_launch.mean()) / (avg_dur_ms * 1e-3) / 1e9
+        peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
+    per_shape = {}
+    for j, (spec, _) in enumerate(gemms):
+        key = f"{spec.M}x{spec.K}x{spec.N}"
+        per_shape.setdefault(key, []).append(durs[:, j].mean())
+    per_shape_us = {k: round(float(np.mean(v)) * 1e3, 3) for k, v in per_shape.items()}
+    log(f"dominant kernel: avg launch {avg_dur_ms * 1e3:.2f} us, {achieved:.1f} {unit}; per shape (us): {per_shape_us}")
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_sha256_16") == source_hash() and tr.get("workload") == args.workload:
+            traffic = tr.get("hbm_bytes_per_launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        threads = len(os.sched_getaffinity(0))
+        t1 = time.perf_counter()
+        nbytes = 0
+        for spec, x in host_sample:
+            Wq = x.Wq if x.Wq is not None else orc.pack(x.q)
+            orc.gemm(x.A, Wq, x.S, x.Z, threads=threads)
+            nbytes += spec.weight_bytes
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(host_sample)} GEMMs (the first layer, every column) of {args.workload}, "
+                         f"{nbytes / 1e6:.1f} MB of weights in {dt:.2f} s"}
+        log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads ({dt:.2f} s)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "tflops": round(tflops, 3),
+        "config": {
+            "workload": args.workload,
+            "gemms_per_step": len(gemms),
+            "M": sorted({s.M for s, _ in gemms}),
+            "weight_bytes_per_step": wl.weight_bytes,
+            "hip_graph": graph is not None,
+        },
+        "roofline": {
+            "bound": bound,
+            "kernel": "w4a16_small_m_kernel",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(avg_dur_ms * 1e3, 3),
+            "per_shape_us": per_shape_us,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,99 @@
+/*
+ * w4a16.h -- C ABI of the group-wise INT4 weight-only GEMM (W4A16) for AMD MI355X (gfx950).
+ *
+ * The operation.  "The Free Half of Speculative Decoding" (third paragraph) quantizes the
+ * target model of a speculative decoder to INT4 with AWQ; "When Do Quantized Drafts Help
+ * Speculative Decoding?" ("Current pilot setup", "What is included") runs GPTQ INT4 drafts
+ * through a W4A16 kernel and verifies gamma+1 = 5 drafted positions per target forward.
+ * Every linear layer of those forwards is the product computed here.  The pages do not
+ * print the dequantization rule or the storage layout; this library uses the plainest
+ * asymmetric group-wise reading, with groups of 128 along K:
+ *
+ *     W[k,n] = (q[k,n] - z[g,n]) * s[g,n],   g = floor(k / 128)
+ *     C[m,n] = sum_k A[m,k] * W[k,n]
+ *
+ * Storage (all arrays dense, row-major, in device memory owned by the caller):
+ *     A_bf16     [M, K]      bfloat16
+ *     Wq         [K/8, N]    uint32; nibble j (bits 4j..4j+3) of Wq[kb,n] is q[8kb+j, n]
+ *     scales_f16 [K/128, N]  IEEE binary16
+ *     zeros_u4   [K/128, N]  one byte per entry, only the low nibble is read
+ *     C          [M, N]      float32, overwritten
+ *
+ * Accuracy contract: every element satisfies
+ *     |C - C_exact| <= 1e-4 * sum_k |A[m,k] * W[k,n]| + 1e-6.
+ * The (q - z) factors and their products with A are exact; partial sums are float32.
+ *
+ * All entry points validate their arguments on the host before any HIP call and return a
+ * status; launches are asynchronous on the given stream (NULL = the null stream), so device
+ * faults surface at the caller's next synchronization.  No entry point synchronizes the
+ * host in steady state.  Inputs must not alias C.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum w4_status {
+    W4_OK = 0,
+    W4_ERR_NULL = 1,      /* a required pointer is NULL                                    */
+    W4_ERR_SHAPE = 2,     /* a size is out of range (see each entry point)                 */
+    W4_ERR_ALIGN = 3,     /* a pointer is not aligned as required                           */
+    W4_ERR_DEVICE = 4,    /* no HIP device, or the current device is not gfx950            */
+    W4_ERR_HIP = 5,       /* a HIP runtime call or launch failed; see w4_last_error()      */
+    W4_ERR_WORKSPACE = 6  /* the split-K workspace would have to grow while the stream is
+                             being captured into a graph: run the same shape once before
+                             capturing                                                      */
+} w4_status;
+
+/*
+ * C = A . W for the group-wise INT4 format above (the verify and draft linear layers of
+ * "When Do Quantized Drafts Help Speculative Decoding?", "Current pilot setup").
+ *
+ *   M >= 1 rows of A (tokens), K >= 128 with K % 128 == 0, N >= 1 columns.
+ *   A_bf16, Wq and C must be 16-byte aligned (W4_ERR_ALIGN otherwise); scales_f16 2-byte.
+ *   Any N is accepted; N % 4 == 0 with 8-byte aligned scales and 4-byte aligned zeros
+ *   takes the vectorized load path.
+ *   Split-K shapes use a library workspace owned per (device, stream): it is allocated on
+ *   first need (outside graph capture) and kept until the process ends.  Calls that may run
+ *   concurrently on different streams each get their own workspace.
+ *   stream: a hipStream_t, or NULL.
+ */
+w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_f16,
+                     const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N,
+                     void *stream);
+
+/*
+ * Packs 4-bit codes into the storage layout: Wq[kb,n] = sum_j (q[8kb+j,n] & 0xF) << 4j.
+ *   q_u4: [K, N] bytes (high nibbles ignored); Wq: [K/8, N] uint32, overwritten.
+ *   K >= 8 with K % 8 == 0, N >= 1; Wq must be 4-byte aligned.  Bit-exact.
+ */
+w4_status w4_pack(const uint8_t *q_u4, uint32_t *Wq, int64_t K, int64_t N, void *stream);
+
+/* How w4a16_gemm would run a shape (host only, no HIP call). */
+typedef struct w4_plan {
+    int kernel;             /* 1 = small-M kernel (M-blocks of 16 rows)                     */
+    int m_blocks;           /* row blocks of 16                                             */
+    int n_tiles;            /* column tiles of 64                                           */
+    int splits;             /* K splits across workgroups (1 = no workspace)                */
+    int groups_per_split;   /* 128-wide K groups handled by one workgroup                   */
+    int64_t workgroups;     /* grid size                                                     */
+    int64_t workspace_bytes;/* split-K workspace needed (0 when splits == 1)                 */
+} w4_plan;
+
+w4_status w4a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out);
+
+/* Static text for a status code. */
+const char *w4_status_string(w4_status s);
+
+/* Text describing the last failure on the calling thread ("" if none). */
+const char *w4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,171 @@
+"""Python binding of libw4a16.so: the group-wise INT4 weight-only GEMM for MI355X (gfx950).
+
+Argument marshalling only: torch tensors supply device pointers and the current HIP
+stream; every step of the computation runs in the library's HIP kernels. Importing this
+package fails loudly when the library has not been built (there is no fallback).
+
+    import int4_weight_only_gemm_amd as w4
+    Wq = w4.pack(q_u8)                    # [K, N] uint8 codes -> [K/8, N] int32 words
+    C = w4.gemm(A_bf16, Wq, s_f16, z_u8)  # [M, N] float32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, List, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "w4a16.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m int4_weight_only_gemm_amd.build` "
+        "(hipcc --offload-arch=gfx950); there is no CPU fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+STATUS = {
+    0: "W4_OK",
+    1: "W4_ERR_NULL",
+    2: "W4_ERR_SHAPE",
+    3: "W4_ERR_ALIGN",
+    4: "W4_ERR_DEVICE",
+    5: "W4_ERR_HIP",
+    6: "W4_ERR_WORKSPACE",
+}
+
+
+class W4Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        detail = _lib.w4_last_error().decode(errors="replace")
+        name = STATUS.get(code, str(code))
+        super().__init__(f"{where}: {name}: {detail}")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_int),
+        ("m_blocks", ctypes.c_int),
+        ("n_tiles", ctypes.c_int),
+        ("splits", ctypes.c_int),
+        ("groups_per_split", ctypes.c_int),
+        ("workgroups", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+    def as_dict(self) -> Dict[str, int]:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_lib.w4a16_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+_lib.w4a16_gemm.restype = ctypes.c_int
+_lib.w4_pack.argtypes = [_vp, _vp, _i64, _i64, _vp]
+_lib.w4_pack.restype = ctypes.c_int
+_lib.w4a16_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(Plan)]
+_lib.w4a16_plan.restype = ctypes.c_int
+_lib.w4_status_string.argtypes = [ctypes.c_int]
+_lib.w4_status_string.restype = ctypes.c_char_p
+_lib.w4_last_error.argtypes = []
+_lib.w4_last_error.restype = ctypes.c_char_p
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def header_functions(path: str = HEADER) -> List[str]:
+    """Names of the functions declared in include/w4a16.h."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\**\s*\b(w4\w*)\s*\(", text, flags=re.M)
+
+
+def status_string(code: int) -> str:
+    return _lib.w4_status_string(code).decode()
+
+
+def plan(M: int, K: int, N: int) -> Dict[str, int]:
+    p = Plan()
+    rc = _lib.w4a16_plan(M, K, N, ctypes.byref(p))
+    if rc:
+        raise W4Error(rc, "w4a16_plan")
+    return p.as_dict()
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(t, name, dtype, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def gemm(A, Wq, scales, zeros, out=None, stream=None):
+    """C[M,N] = A[M,K] . W[K,N] with W[k,n] = (q[k,n] - z[k/128,n]) * s[k/128,n].
+
+    A: bfloat16 [M,K]; Wq: int32 (or uint32) [K/8,N] packed codes; scales: float16
+    [K/128,N]; zeros: uint8 [K/128,N]; out: optional float32 [M,N] (overwritten).
+    """
+    import torch
+    _check(A, "A", torch.bfloat16, 2)
+    if Wq.dtype not in (torch.int32, torch.uint32):
+        raise TypeError("Wq must be int32 or uint32")
+    _check(Wq, "Wq", Wq.dtype, 2)
+    _check(scales, "scales", torch.float16, 2)
+    _check(zeros, "zeros", torch.uint8, 2)
+    M, K = A.shape
+    N = Wq.shape[1]
+    if Wq.shape[0] * 8 != K or scales.shape != (K // 128, N) or zeros.shape != (K // 128, N):
+        raise ValueError(f"inconsistent shapes A{tuple(A.shape)} Wq{tuple(Wq.shape)} "
+                         f"scales{tuple(scales.shape)} zeros{tuple(zeros.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        _check(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    rc = _lib.w4a16_gemm(A.data_ptr(), Wq.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                         out.data_ptr(), M, K, N, _stream_handle(stream))
+    if rc:
+        raise W4Error(rc, "w4a16_gemm")
+    return out
+
+
+def gemm_raw(A_ptr: int, Wq_ptr: int, S_ptr: int, Z_ptr: int, C_ptr: int, M: int, K: int, N: int,
+             stream_handle: int = 0) -> None:
+    """Direct C-ABI call on raw device pointers (no checks beyond the library's own)."""
+    rc = _lib.w4a16_gemm(A_ptr, Wq_ptr, S_ptr, Z_ptr, C_ptr, M, K, N, stream_handle)
+    if rc:
+        raise W4Error(rc, "w4a16_gemm")
+
+
+def pack(q, out=None, stream=None):
+    """Pack uint8 codes [K,N] (high nibbles ignored) into int32 words [K/8,N]."""
+    import torch
+    _check(q, "q", torch.uint8, 2)
+    K, N = q.shape
+    if out is None:
+        out = torch.empty((K // 8, N), dtype=torch.int32, device=q.device)
+    elif out.dtype not in (torch.int32, torch.uint32) or tuple(out.shape) != (K // 8, N):
+        raise ValueError("out must be int32 [K/8, N]")
+    rc = _lib.w4_pack(q.data_ptr(), out.data_ptr(), K, N, _stream_handle(stream))
+    if rc:
+        raise W4Error(rc, "w4_pack")
+    return out

@@ -1,0 +1,92 @@
+"""Host-side checks of the C-ABI library (no kernel launches, no GPU needed).
+
+Every call here fails argument validation, which the library performs on the host before
+any HIP call, so nothing reaches the device.
+"""
+import ctypes
+import os
+
+import pytest
+
+import int4_weight_only_gemm_amd as w4
+
+
+def test_library_exports_every_declared_symbol():
+    names = w4.header_functions()
+    assert set(names) >= {"w4a16_gemm", "w4_pack", "w4a16_plan", "w4_status_string", "w4_last_error"}
+    lib = w4.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/w4a16.h but not exported"
+
+
+def test_status_strings():
+    for code in range(7):
+        s = w4.status_string(code)
+        assert s and s != "unknown status"
+    assert w4.status_string(99) == "unknown status"
+
+
+A16, W16, S8, Z4, C16 = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000  # never dereferenced
+
+
+def _gemm(*args):
+    return w4.lib().w4a16_gemm(*args)
+
+
+@pytest.mark.parametrize("ptrs", [
+    (None, W16, S8, Z4, C16), (A16, None, S8, Z4, C16), (A16, W16, None, Z4, C16),
+    (A16, W16, S8, None, C16), (A16, W16, S8, Z4, None)])
+def test_null_pointers(ptrs):
+    assert _gemm(*ptrs, 5, 128, 64, None) == 1
+    assert w4.lib().w4_last_error()
+
+
+@pytest.mark.parametrize("mkn", [(0, 128, 64), (5, 0, 64), (5, 64, 64), (5, 129, 64), (5, 200, 64),
+                                 (5, 128, 0), (-1, 128, 8), (5, -128, 8), (1 << 31, 1 << 20, 1 << 20)])
+def test_bad_shapes(mkn):
+    assert _gemm(A16, W16, S8, Z4, C16, *mkn, None) == 2
+
+
+@pytest.mark.parametrize("ptrs", [
+    (A16 + 2, W16, S8, Z4, C16), (A16, W16 + 4, S8, Z4, C16), (A16, W16, S8, Z4, C16 + 8),
+    (A16, W16, S8 + 1, Z4, C16)])
+def test_misaligned(ptrs):
+    assert _gemm(*ptrs, 5, 128, 64, None) == 3
+
+
+def test_pack_validation():
+    lib = w4.lib()
+    assert lib.w4_pack(None, W16, 8, 4, None) == 1
+    assert lib.w4_pack(A16, None, 8, 4, None) == 1
+    assert lib.w4_pack(A16, W16, 12, 4, None) == 2
+    assert lib.w4_pack(A16, W16, 0, 4, None) == 2
+    assert lib.w4_pack(A16, W16, 8, 0, None) == 2
+    assert lib.w4_pack(A16, W16 + 2, 8, 4, None) == 3
+
+
+def test_plan_covers_shapes():
+    # every shape of the synthetic workloads has a valid plan that tiles N and K exactly
+    import synth
+    seen = set()
+    for wl in synth.WORKLOADS.values():
+        for g in wl.gemms:
+            key = (g.M, g.K, g.N)
+            if key in seen:
+                continue
+            seen.add(key)
+            p = w4.plan(*key)
+            groups = g.K // 128
+            assert p["n_tiles"] * 64 >= g.N > (p["n_tiles"] - 1) * 64
+            assert p["m_blocks"] * 16 >= g.M > (p["m_blocks"] - 1) * 16
+            assert p["splits"] * p["groups_per_split"] >= groups
+            assert (p["splits"] - 1) * p["groups_per_split"] < groups
+            assert p["workgroups"] == p["n_tiles"] * p["m_blocks"] * p["splits"]
+            assert (p["workspace_bytes"] > 0) == (p["splits"] > 1)
+    with pytest.raises(w4.W4Error):
+        w4.plan(5, 100, 64)
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present")
+def test_no_device_is_reported():
+    # valid arguments on a host with no GPU: the device check fails before any launch
+    assert _gemm(A16, W16, S8, Z4, C16, 5, 128, 64, None) == 4

@@ -1,0 +1,280 @@
+"""HIP path against the oracle, element by element, through the C-ABI (needs gfx950).
+
+Tolerance (per element, float64): |C_gpu - C_oracle| <= 1e-4 * sum_k |A[m,k] W[k,n]| + 1e-6.
+Packing is compared bit for bit. Cases that are exact in float32 (one-hot A, q = z, s = 0)
+are compared bit for bit as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_gemm_amd as w4
+import oracle
+import synth
+from gpu_helpers import check, host_words, log, run, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+# ------------------------------------------------------------------------------ packing
+@pytest.mark.parametrize("K,N", [(8, 1), (16, 3), (128, 64), (384, 257), (1536, 1536), (1024, 4099)])
+def test_pack_bit_exact(orc, K, N):
+    log(f"pack K={K} N={N}")
+    r = np.random.default_rng(K * 7 + N)
+    q = r.integers(0, 256, size=(K, N), dtype=np.uint8)  # garbage high nibbles included
+    q[0, 0], q[-1, -1] = 0x0F, 0xF0
+    Wq = w4.pack(torch.from_numpy(q).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(Wq.cpu().numpy().view(np.uint32), orc.pack(q))
+
+
+# ------------------------------------------------------------------- tiny-shape grid
+GRID_M = [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 17, 63, 64, 65, 160]
+GRID_K = [128, 256, 384, 1152]
+GRID_N = [1, 3, 7, 8, 63, 64, 65, 257]
+
+
+@pytest.mark.parametrize("M", GRID_M)
+def test_grid(orc, M):
+    worst = 0.0
+    for K in GRID_K:
+        for N in GRID_N:
+            log(f"grid M={M} K={K} N={N}")
+            x = synth.generate_custom(M, K, N, seed=1)
+            dev = to_dev(x)
+            C = run(dev).cpu().numpy()
+            Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
+            worst = max(worst, check(C, Cr, Cabs, f"M={M} K={K} N={N}"))
+    log(f"grid M={M}: worst error / bound = {worst:.3g}")
+
+
+@pytest.mark.parametrize("M,K,N", [(5, 4096, 64), (1, 18944, 100), (7, 8192, 200), (16, 2048, 36),
+                                   (3, 11008, 4096), (160, 1024, 130)])
+def test_split_k_shapes(orc, M, K, N):
+    p = w4.plan(M, K, N)
+    log(f"split-K M={M} K={K} N={N} plan={p}")
+    x = synth.generate_custom(M, K, N, seed=2)
+    C = run(to_dev(x)).cpu().numpy()
+    cols = np.unique(np.r_[0, N - 1, np.random.default_rng(3).integers(0, N, 64)])
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+    check(C[:, cols], Cr, Cabs, f"split M={M} K={K} N={N}")
+
+
+# ----------------------------------------------------------------- exact special cases
+@pytest.mark.parametrize("M,K,N", [(5, 384, 72), (16, 1152, 64), (1, 4096, 33)])
+def test_one_hot_bitwise(orc, M, K, N):
+    x = synth.generate_custom(M, K, N, seed=4)
+    dev = to_dev(x)
+    r = np.random.default_rng(5)
+    for (m0, k0) in ((0, 0), (M - 1, K - 1), (M // 2, 131), (0, K // 2 + 5)):
+        a0 = np.float32(r.choice([1.0, -2.5, 0.375, 96.0, -0.0078125, 3.0e4, 1.0e-3]))
+        A = np.zeros((M, K), np.float32)
+        A[m0, k0] = a0
+        Ab = synth.f32_to_bf16_bits(A)
+        log(f"one-hot M={M} K={K} N={N} m0={m0} k0={k0} a0={a0}")
+        dev["A"] = torch.from_numpy(Ab.view(np.int16)).cuda().view(torch.bfloat16)
+        C = run(dev).cpu().numpy().astype(np.float64)
+        Cr, _ = orc.gemm(Ab, x.Wq, x.S, x.Z)
+        assert np.array_equal(C, Cr), f"one-hot ({m0},{k0}) differs"
+
+
+def test_zero_cases_exact(orc):
+    M, K, N = 7, 1152, 129
+    x = synth.generate_custom(M, K, N, seed=6)
+    q = np.repeat(x.Z, 128, axis=0).astype(np.uint8)
+    x_eq = synth.GemmInputs(A=x.A, Wq=orc.pack(q), q=None, S=x.S, Z=x.Z)
+    log("zero case q == z")
+    C = run(to_dev(x_eq)).cpu().numpy()
+    assert np.all(C == 0.0)
+    x_s0 = synth.GemmInputs(A=x.A, Wq=x.Wq, q=None, S=np.zeros_like(x.S), Z=x.Z)
+    log("zero case s == 0")
+    C = run(to_dev(x_s0)).cpu().numpy()
+    assert np.all(C == 0.0)
+
+
+def test_zero_high_nibble_ignored(orc):
+    M, K, N = 5, 512, 96
+    x = synth.generate_custom(M, K, N, seed=7)
+    dev = to_dev(x)
+    C1 = run(dev).cpu().numpy()
+    dev["Z"] = dev["Z"] | 0xB0
+    log("zero points with high nibbles set")
+    C2 = run(dev).cpu().numpy()
+    assert np.array_equal(C1, C2)
+
+
+def test_identity_rowsum(orc):
+    # q = z + 1, s = 1: every column is the row sum of A
+    M, K, N = 5, 3584, 64
+    r = np.random.default_rng(8)
+    x = synth.generate_custom(M, K, N, seed=8)
+    Z = r.integers(0, 15, size=x.Z.shape, dtype=np.uint8)
+    q = np.repeat(Z + 1, 128, axis=0).astype(np.uint8)
+    S = np.ones(x.S.shape, np.float16).view(np.uint16)
+    xi = synth.GemmInputs(A=x.A, Wq=orc.pack(q), q=None, S=S, Z=Z)
+    log("identity q = z + 1, s = 1")
+    C = run(to_dev(xi)).cpu().numpy()
+    Cr, Cabs = orc.gemm(xi.A, xi.Wq, xi.S, xi.Z)
+    check(C, Cr, Cabs, "identity")
+    assert np.all(C == C[:, :1])  # all columns identical
+
+
+def test_activation_dynamic_range(orc):
+    # rows of very large and very small bf16 magnitudes (beyond fp16 range) stay exact
+    M, K, N = 6, 512, 64
+    x = synth.generate_custom(M, K, N, seed=9)
+    a = (x.A.astype(np.uint32) << 16).view(np.float32)
+    scale = np.array([1e30, 1e-30, 7e4, 1e-6, 1.0, 3e-38], np.float32)[:, None]
+    A = synth.f32_to_bf16_bits(a * scale)
+    xs = synth.GemmInputs(A=A, Wq=x.Wq, q=None, S=x.S, Z=x.Z)
+    log("activation dynamic range rows")
+    C = run(to_dev(xs)).cpu().numpy()
+    Cr, Cabs = orc.gemm(xs.A, xs.Wq, xs.S, xs.Z)
+    check(C, Cr, Cabs, "dynamic range")
+
+
+def test_error_well_inside_tolerance(orc):
+    # exact (q - z) products and float32 partials keep the error under ~2e-5 of sum|A W|
+    M, K, N = 5, 18944, 256
+    x = synth.generate_custom(M, K, N, seed=10)
+    log("error bound at K=18944")
+    C = run(to_dev(x)).cpu().numpy().astype(np.float64)
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
+    rel = np.abs(C - Cr) / Cabs
+    assert rel.max() < 2e-5, rel.max()
+
+
+# ----------------------------------------------------------- workspace, poison, graphs
+def test_poisoned_output_fully_written(orc):
+    for (M, K, N) in ((5, 1536, 1536), (5, 18944, 192), (17, 256, 70)):
+        x = synth.generate_custom(M, K, N, seed=11)
+        dev = to_dev(x)
+        out = torch.full((M, N), float("nan"), device="cuda")
+        log(f"poisoned C M={M} K={K} N={N}")
+        C = run(dev, out=out).cpu().numpy()
+        assert np.all(np.isfinite(C))
+        cols = np.arange(0, N, max(1, N // 50))
+        Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+        check(C[:, cols], Cr, Cabs, "poisoned")
+
+
+def test_back_to_back_shapes_reproducible(orc):
+    shapes = [(5, 18944, 3584), (5, 3584, 3584), (1, 8960, 1536), (5, 18944, 3584)]
+    devs = {}
+    results = []
+    for (M, K, N) in shapes:
+        if (M, K, N) not in devs:
+            devs[(M, K, N)] = (synth.generate_custom(M, K, N, seed=12),)
+            devs[(M, K, N)] += (to_dev(devs[(M, K, N)][0]),)
+        log(f"back-to-back M={M} K={K} N={N}")
+        results.append(run(devs[(M, K, N)][1]))
+    torch.cuda.synchronize()
+    assert torch.equal(results[0], results[3]), "split-K result not reproducible"
+    for (M, K, N), C in zip(shapes[:3], results[:3]):
+        x = devs[(M, K, N)][0]
+        cols = np.arange(0, N, 61)
+        Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+        check(C.cpu().numpy()[:, cols], Cr, Cabs, f"b2b {M}x{K}x{N}")
+
+
+def test_graph_replay_matches_eager():
+    shapes = [(5, 3584, 4608), (5, 18944, 3584), (1, 1536, 17920)]
+    xs = [to_dev(synth.generate_custom(M, K, N, seed=13)) for (M, K, N) in shapes]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        eager = [run(d).clone() for d in xs]  # also sizes the workspace for this stream
+    torch.cuda.synchronize()
+    outs = [torch.empty_like(e) for e in eager]
+    g = torch.cuda.CUDAGraph()
+    log("graph capture")
+    with torch.cuda.graph(g, stream=s):
+        for d, o in zip(xs, outs):
+            run(d, out=o)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        log(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1024, 1024, device="cuda") @ torch.randn(1024, 1024, device="cuda")
+        torch.cuda.synchronize()
+        del junk
+        for e, o in zip(eager, outs):
+            assert torch.equal(e, o), f"replay {rep} differs from eager"
+
+
+def test_unaligned_scale_zero_views(orc):
+    # scales/zeros views that are only 2-/1-byte aligned take the scalar load path
+    M, K, N = 5, 512, 128
+    x = synth.generate_custom(M, K, N, seed=14)
+    dev = to_dev(x)
+    G = K // 128
+    s_big = torch.empty(G * N + 1, dtype=torch.float16, device="cuda")
+    s_big[1:] = dev["S"].flatten()
+    z_big = torch.empty(G * N + 1, dtype=torch.uint8, device="cuda")
+    z_big[1:] = dev["Z"].flatten()
+    dev["S"] = s_big[1:].view(G, N)
+    dev["Z"] = z_big[1:].view(G, N)
+    log("unaligned scale/zero views")
+    C = run(dev).cpu().numpy()
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
+    check(C, Cr, Cabs, "unaligned views")
+
+
+def test_misaligned_pointer_rejected():
+    M, K, N = 5, 128, 64
+    A = torch.zeros(M * K + 8, dtype=torch.bfloat16, device="cuda")
+    Wq = torch.zeros(K // 8, N, dtype=torch.int32, device="cuda")
+    S = torch.zeros(K // 128, N, dtype=torch.float16, device="cuda")
+    Z = torch.zeros(K // 128, N, dtype=torch.uint8, device="cuda")
+    C = torch.zeros(M, N, dtype=torch.float32, device="cuda")
+    with pytest.raises(w4.W4Error) as e:
+        w4.gemm_raw(A.data_ptr() + 2, Wq.data_ptr(), S.data_ptr(), Z.data_ptr(), C.data_ptr(), M, K, N)
+    assert e.value.code == 3
+
+
+# ------------------------------------------------ the workloads at full size (sampled)
+def _sampled_check(orc, spec, ncols=48):
+    x = synth.generate(spec)
+    dev = to_dev(x)
+    if "q" in dev:
+        dev["Wq"] = w4.pack(dev["q"])
+    log(f"workload gemm {spec.name} M={spec.M} K={spec.K} N={spec.N} plan={w4.plan(spec.M, spec.K, spec.N)}")
+    C = run(dev).cpu().numpy()
+    assert np.all(np.isfinite(C))
+    r = np.random.default_rng(abs(hash(spec.seed)) % (1 << 32))
+    cols = np.unique(np.r_[0, spec.N - 1, r.integers(0, spec.N, ncols)])
+    Cr, Cabs = orc.gemm(x.A, host_words(x), x.S, x.Z, cols=cols)
+    return check(C[:, cols], Cr, Cabs, spec.name)
+
+
+def test_workload_single_m5_full(orc):
+    spec = synth.WORKLOADS["single-m5-k1536-n1536"].gemms[0]
+    x = synth.generate(spec)
+    dev = to_dev(x)
+    dev["Wq"] = w4.pack(dev["q"])
+    log("single M=5 K=N=1536, every element")
+    C = run(dev).cpu().numpy()
+    Cr, Cabs = orc.gemm(x.A, orc.pack(x.q), x.S, x.Z)
+    check(C, Cr, Cabs, "single-m5")
+
+
+@pytest.mark.parametrize("name", ["qwen2.5-1.5b-draft-m1", "qwen2.5-7b-verify-m5", "llama2-7b-batched-verify-m160"])
+def test_workload_layer_sampled(orc, name):
+    wl = synth.WORKLOADS[name]
+    for spec in wl.gemms[:4]:  # one layer: every projection shape of the model
+        _sampled_check(orc, spec)
+    _sampled_check(orc, wl.gemms[-1])  # and the last GEMM of the pass
+
+
+def test_workload_gamma_sweep_sampled(orc):
+    wl = synth.WORKLOADS["qwen2.5-7b-gamma-sweep"]
+    for M in (3, 4, 5, 6, 7):
+        for spec in [g for g in wl.gemms if g.M == M][:2]:
+            _sampled_check(orc, spec, ncols=24)
