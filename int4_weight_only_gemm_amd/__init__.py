@@ -24,6 +24,12 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -m int4_weight_only_gemm_amd.build` "
         "(hipcc --offload-arch=gfx950); there is no CPU fallback")
 
+# One HIP runtime per process: torch bundles its own libamdhip64.so.7 (and HSA runtime).
+# Importing torch first makes the library's libamdhip64.so.7 dependency resolve to that
+# already-loaded copy; loading the library first would bring in /opt/rocm's copy and torch
+# would then start a second, conflicting runtime.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 STATUS = {

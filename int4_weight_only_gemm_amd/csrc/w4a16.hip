@@ -16,14 +16,16 @@
 //    mantissa of 1024.0 (or of 1024.0 + 16 q for the odd nibble of a byte) and the zero
 //    point is removed with one packed fp16 add/fma.  That is 9 VALU ops per 8 weights.
 //  * The products run on the matrix cores (v_mfma_f32_16x16x32_f16).  The activation tile
-//    is converted from bfloat16 to binary16 in LDS with a power-of-two scale per 128-wide
-//    group, chosen so the group's largest magnitude lands in [2^15, 2^16); the scale is
-//    undone exactly when the group's float32 partial is rescaled by s.  Every product
-//    a*(q-z) is then exact; bfloat16 values more than 2^29 below their group's maximum
-//    may be flushed (error below 2^-29 of that maximum per element).
-//  * Split-K across workgroups writes float32 partials to a workspace; a per-tile arrival
-//    counter elects the last workgroup, which sums the partials in split order, writes C
-//    and resets the counter.  One launch per GEMM, no memset, bitwise reproducible.
+//    is converted from bfloat16 to binary16 in LDS with a power-of-two scale per row and
+//    128-wide group, chosen so that row's largest magnitude in the group lands in
+//    [2^15, 2^16); the scale is undone exactly when the group's float32 partial is
+//    rescaled by s.  Every product a*(q-z) is then exact; bfloat16 values more than 2^29
+//    below the largest magnitude of their row within the group may be flushed (error
+//    below 2^-29 of that maximum per element).
+//  * Split-K across workgroups writes float32 partials to a workspace with device-coherent
+//    stores; a per-tile arrival counter elects the last workgroup, which sums the partials
+//    in split order, writes C and resets the counter.  One launch per GEMM, no memset, no
+//    cache flush, bitwise reproducible.
 
 #include <hip/hip_runtime.h>
 
@@ -54,12 +56,12 @@ constexpr int kTileN = 64;                 // output columns per workgroup (16 l
 constexpr int kTileM = 16;                 // output rows per M-block (one MFMA tile)
 constexpr int kGroup = 128;                // quantization group along K
 constexpr int kChunksPerRow = kGroup / 8;  // 16-byte activation chunks per group row
-constexpr int kLdsRowChunks = kChunksPerRow + 1;  // +1 chunk of padding: conflict-free reads
-constexpr int kLdsWaveBytes = kTileM * kLdsRowChunks * 16;
-constexpr int kLdsBufBytes = kWaves * kLdsWaveBytes;
+constexpr int kARowBytes = (kChunksPerRow + 1) * 16;  // +16 bytes of padding: conflict-free reads
+constexpr int kMaxChunksPerThread = 12;     // activation slice <= 12 x 256 chunks (51 KiB of LDS)
+constexpr int kMaxSliceRowGroups = kMaxChunksPerThread * kThreads / kChunksPerRow;  // rows x groups
 constexpr int kRedBytes = kWaves * kTileM * kTileN * 4;
-constexpr int kLdsBytes = (2 * kLdsBufBytes > kRedBytes) ? 2 * kLdsBufBytes : kRedBytes;
-constexpr int kTargetWorkgroups = 512;
+constexpr int kTargetWorkgroups = 768;  // 256 CUs x 3 resident workgroups (3 waves per SIMD)
+constexpr int kCacheStream = 2;         // buffer-load cache policy: non-temporal (streamed once)
 
 struct SmallParams {
     const uint16_t *A;
@@ -135,13 +137,6 @@ __device__ __forceinline__ u32x4 convert_chunk(u32x4 v, int x)
     return r;
 }
 
-__device__ __forceinline__ int wave_max(int v)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, kWave));
-    return v;
-}
-
 // Maps the hardware workgroup id to a logical id so that logically consecutive
 // workgroups (the K splits of one tile) are dispatched to the same XCD: workgroup b runs
 // on XCD b % 8.
@@ -152,65 +147,90 @@ __device__ __forceinline__ uint32_t xcd_local_id(uint32_t b, uint32_t n)
 }
 
 // ------------------------------------------------------------------------------------
-// Per-group register set of one wave: 4 packed rows (one 16-byte load per lane each),
-// the group's scales and zeros for the lane's 4 columns, and up to 4 activation chunks.
+// Register slot of one wave for one group: 4 packed rows (one 16-byte load per lane each)
+// and the group's scales and zeros for the lane's 4 columns.
 struct GroupRegs {
     u32x4 w[4];
     u32x2 s;      // 4 binary16 scales
     uint32_t z;   // 4 zero bytes
-    u32x4 a[4];
 };
 
+// Per-lane byte offsets that stay fixed for a whole workgroup.  All loads are buffer
+// loads: a scalar resource (base, size) per array, this per-lane offset, and a
+// wave-uniform scalar offset per group, so a group's loads cost no address VGPRs.
+// Out-of-range columns read a clamped in-range address (those values are never stored)
+// and no load sits behind a branch, so the compiler waits for exactly the slot it needs
+// while later groups stay in flight.
 template <bool VEC>
-__device__ __forceinline__ void load_group(const SmallParams &p, int g, int n0, int m0, int mv,
-                                           int lane, GroupRegs &r)
+struct LaneOffsets {
+    uint32_t w[VEC ? 1 : 4];  // packed words: row kq of the group, this lane's column(s)
+    uint32_t s[VEC ? 1 : 4];  // scales
+    uint32_t z[VEC ? 1 : 4];  // zeros
+};
+
+struct Resources {
+    __amdgpu_buffer_rsrc_t W, S, Z, A;
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords
+
+template <bool VEC>
+__device__ __forceinline__ void lane_offsets(const SmallParams &p, int n0, int lane, LaneOffsets<VEC> &o)
 {
     const int c = lane & 15, kq = lane >> 4;
     const int64_t N = p.N;
     const int64_t col = n0 + 4 * c;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int64_t row = (int64_t)g * 16 + 4 * st + kq;
-        const uint32_t *src = p.Wq + row * N + col;
-        if (VEC) {
-            r.w[st] = (col < N) ? __builtin_nontemporal_load((const u32x4 *)src) : u32x4{0, 0, 0, 0};
-        } else {
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                r.w[st][t] = (col + t < N) ? __builtin_nontemporal_load(src + t) : 0u;
-        }
-    }
-    const int64_t gi = (int64_t)g * N + col;
     if (VEC) {
-        r.s = (col < N) ? *(const u32x2 *)(p.S + gi) : u32x2{0, 0};
-        r.z = (col < N) ? *(const uint32_t *)(p.Z + gi) : 0u;
+        const int64_t colv = col < N - 4 ? col : N - 4;  // N % 4 == 0, so N >= 4
+        o.w[0] = (uint32_t)((kq * N + colv) * 4);
+        o.s[0] = (uint32_t)(colv * 2);
+        o.z[0] = (uint32_t)colv;
     } else {
-        uint32_t s01 = 0, s23 = 0, zz = 0;
-        if (col + 0 < N) { s01 |= p.S[gi + 0]; zz |= (uint32_t)p.Z[gi + 0]; }
-        if (col + 1 < N) { s01 |= (uint32_t)p.S[gi + 1] << 16; zz |= (uint32_t)p.Z[gi + 1] << 8; }
-        if (col + 2 < N) { s23 |= p.S[gi + 2]; zz |= (uint32_t)p.Z[gi + 2] << 16; }
-        if (col + 3 < N) { s23 |= (uint32_t)p.S[gi + 3] << 16; zz |= (uint32_t)p.Z[gi + 3] << 24; }
-        r.s = u32x2{s01, s23};
-        r.z = zz;
-    }
-    // activation chunks: chunk id ch = lane + 64 i -> row ch / 16, chunk ch % 16
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ch = lane + 64 * i;
-        const int rr = ch >> 4, kc = ch & 15;
-        if (rr < mv) {
-            const uint16_t *src = p.A + (int64_t)(m0 + rr) * p.K + (int64_t)g * kGroup + kc * 8;
-            r.a[i] = *(const u32x4 *)src;
-        } else {
-            r.a[i] = u32x4{0, 0, 0, 0};
+        for (int t = 0; t < 4; ++t) {
+            const int64_t ct = col + t < N ? col + t : N - 1;
+            o.w[t] = (uint32_t)((kq * N + ct) * 4);
+            o.s[t] = (uint32_t)(ct * 2);
+            o.z[t] = (uint32_t)ct;
         }
     }
 }
 
-// One group of one wave: activation staging (already in LDS), 4 MFMA steps per column
-// subtile, then acc += s * 2^-x * P.
-__device__ __forceinline__ void compute_group(const GroupRegs &r, const char *lds_wave, int x,
-                                              int mv, int lane, f32x4 (&acc)[4])
+template <bool VEC>
+__device__ __forceinline__ void load_group(const SmallParams &p, const Resources &rs,
+                                           const LaneOffsets<VEC> &o, int g, GroupRegs &r)
+{
+    const uint32_t rowbytes = (uint32_t)p.N * 4;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const uint32_t so = ((uint32_t)g * 16 + 4 * st) * rowbytes;
+        if (VEC) {
+            r.w[st] = __builtin_amdgcn_raw_buffer_load_b128(rs.W, o.w[0], so, kCacheStream);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) r.w[st][t] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, o.w[t], so, kCacheStream);
+        }
+    }
+    const uint32_t gso = (uint32_t)g * (uint32_t)p.N;
+    if (VEC) {
+        r.s = __builtin_amdgcn_raw_buffer_load_b64(rs.S, o.s[0], gso * 2, 0);
+        r.z = __builtin_amdgcn_raw_buffer_load_b32(rs.Z, o.z[0], gso, 0);
+    } else {
+        uint32_t sv[4], zv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sv[t] = __builtin_amdgcn_raw_buffer_load_b16(rs.S, o.s[t], gso * 2, 0);
+            zv[t] = __builtin_amdgcn_raw_buffer_load_b8(rs.Z, o.z[t], gso, 0);
+        }
+        r.s = u32x2{sv[0] | (sv[1] << 16), sv[2] | (sv[3] << 16)};
+        r.z = zv[0] | (zv[1] << 8) | (zv[2] << 16) | (zv[3] << 24);
+    }
+}
+
+// One group of one wave: 4 MFMA steps per column subtile into the group partial P, then
+// acc += s * P (the activation tile is in LDS, scaled per row by 2^x).
+__device__ __forceinline__ void compute_group(const GroupRegs &r, const char *lds_group, int mv, int lane,
+                                              f32x4 (&acc)[4])
 {
     const int c = lane & 15, kq = lane >> 4;
     uint32_t magic;
@@ -229,13 +249,8 @@ __device__ __forceinline__ void compute_group(const GroupRegs &r, const char *ld
     for (int t = 0; t < 4; ++t) P[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-        f16x8 a_op;
-        if (c < mv) {
-            const u32x4 av = *(const u32x4 *)(lds_wave + (c * kLdsRowChunks + 4 * st + kq) * 16);
-            a_op = __builtin_bit_cast(f16x8, av);
-        } else {
-            a_op = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
-        }
+        f16x8 a_op = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
+        if (c < mv) a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_group + c * kARowBytes + (4 * st + kq) * 16));
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const f16x8 b_op = unpack8(r.w[st][t], zlo[t], zhi[t], magic);
@@ -245,35 +260,68 @@ __device__ __forceinline__ void compute_group(const GroupRegs &r, const char *ld
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
-        const float sc = ldexpf((float)__builtin_bit_cast(_Float16, sb), -x);
+        const float sv = (float)__builtin_bit_cast(_Float16, sb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(sc, P[t][i], acc[t][i]);
+        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(sv, P[t][i], acc[t][i]);
     }
 }
 
-// Stage the wave's group of activations into LDS as scaled binary16; return the scale
-// exponent x (the group's values were multiplied by 2^x).
-__device__ __forceinline__ int stage_activations(const GroupRegs &r, char *lds_wave, int mv, int lane)
+// Workgroup-wide barrier for LDS only: waits for this wave's LDS operations, not for its
+// global loads, so the weight loads already in flight stay in flight.
+__device__ __forceinline__ void lds_barrier()
 {
-    int e = 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Stage the workgroup's activation slice A[m0 .. m0+mv-1, 128 g_begin .. 128 g_end) into
+// LDS as binary16, row r scaled by 2^x[r] with x[r] = 142 - (largest biased exponent of
+// row r in the slice), which puts the row's largest magnitude in [2^15, 2^16).  Layout:
+// group gl, row r, chunk kc (8 values) at gl*mv*272 + r*272 + kc*16; 16 bytes of padding
+// per row keep the MFMA operand reads free of bank conflicts.  row_e ends up holding the
+// row exponents (0 for rows >= mv).
+__device__ __forceinline__ void stage_slice(const SmallParams &p, const Resources &rs, int m0, int mv,
+                                            int g_begin, int ng, char *lds_a, int *row_e)
+{
+    const int tid = threadIdx.x;
+    const int nch = mv * ng * kChunksPerRow;
+    u32x4 v[kMaxChunksPerThread];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e = max(e, chunk_max_exp(r.a[i]));
-    e = wave_max(e);
-    e = max(e, 1);            // all-zero / subnormal groups use the smallest normal exponent
-    const int x = 142 - e;    // largest magnitude -> [2^15, 2^16)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int ch = lane + 64 * i;
-        const int rr = ch >> 4, kc = ch & 15;
-        if (rr < mv) *(u32x4 *)(lds_wave + (rr * kLdsRowChunks + kc) * 16) = convert_chunk(r.a[i], x);
+    for (int i = 0; i < kMaxChunksPerThread; ++i) {
+        int ch = tid + kThreads * i;
+        ch = ch < nch ? ch : nch - 1;  // branch-free: spare threads reload the last chunk
+        const int kc = ch % kChunksPerRow, gr = ch / kChunksPerRow;
+        const int r = gr % mv, gl = gr / mv;
+        const uint32_t off = (uint32_t)(((int64_t)(m0 + r) * p.K + (int64_t)(g_begin + gl) * kGroup + kc * 8) * 2);
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, off, 0, 0);
     }
-    return x;
+    if (tid < kTileM) row_e[tid] = 1;  // smallest normal exponent: all-zero rows stay at 2^0 scale
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kMaxChunksPerThread; ++i) {
+        const int ch = tid + kThreads * i;
+        if (ch < nch) atomicMax(row_e + (ch / kChunksPerRow) % mv, chunk_max_exp(v[i]));
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < kMaxChunksPerThread; ++i) {
+        const int ch = tid + kThreads * i;
+        if (ch < nch) {
+            const int gr = ch / kChunksPerRow;
+            const int x = 142 - row_e[gr % mv];
+            *(u32x4 *)(lds_a + gr * kARowBytes + (ch % kChunksPerRow) * 16) = convert_chunk(v[i], x);
+        }
+    }
+    lds_barrier();
 }
 
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void w4a16_small_m_kernel(SmallParams p)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void w4a16_small_m_kernel(SmallParams p)
 {
-    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    extern __shared__ __attribute__((aligned(16))) char lds[];  // activation slice, then reduction
+    __shared__ int row_e[kTileM];
     __shared__ int s_last;
 
     const uint32_t logical = xcd_local_id(blockIdx.x, gridDim.x);
@@ -283,43 +331,67 @@ __global__ __launch_bounds__(kThreads) void w4a16_small_m_kernel(SmallParams p)
     const int mb = (int)(tile / (uint32_t)p.n_tiles);
     const int n0 = nt * kTileN, m0 = mb * kTileM;
     const int mv = (p.M - m0 < kTileM) ? (int)(p.M - m0) : kTileM;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
     const int c = lane & 15, kq = lane >> 4;
 
+    // This workgroup's groups are [g_begin, g_end); wave w takes g_begin + w, + 4, ...
     const int g_begin = sp * p.gps;
     const int g_end = min(p.groups, g_begin + p.gps);
-    const int rounds = (g_end - g_begin + kWaves - 1) / kWaves;
+    const int g0 = g_begin + wave;
+    const int n_my = g0 < g_end ? (g_end - g0 + kWaves - 1) / kWaves : 0;
+
+    Resources rs;
+    rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K / 8 * p.N * 4), kRsrcWord3);
+    rs.S = __builtin_amdgcn_make_buffer_rsrc((void *)p.S, (short)0, (int)(p.K / kGroup * p.N * 2), kRsrcWord3);
+    rs.Z = __builtin_amdgcn_make_buffer_rsrc((void *)p.Z, (short)0, (int)(p.K / kGroup * p.N), kRsrcWord3);
+    rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(p.M * p.K * 2), kRsrcWord3);
+    LaneOffsets<VEC> lo;
+    lane_offsets<VEC>(p, n0, lane, lo);
 
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Every wave runs the same number of rounds (barriers are workgroup-wide); a wave
-    // whose group index falls past g_end skips the work of that round.
-    GroupRegs ra, rb;
-    int g = g_begin + wave;
-    if (g < g_end) load_group<VEC>(p, g, n0, m0, mv, lane, ra);
-    for (int rd = 0; rd < rounds; rd += 2) {
-        {
-            const int gn = g + kWaves;
-            if (gn < g_end) load_group<VEC>(p, gn, n0, m0, mv, lane, rb);
-            char *buf = lds + (rd & 1) * kLdsBufBytes + wave * kLdsWaveBytes;
-            int x = 0;
-            if (g < g_end) x = stage_activations(ra, buf, mv, lane);
-            __syncthreads();
-            if (g < g_end) compute_group(ra, buf, x, mv, lane, acc);
-            g = gn;
+    // The first group's weights are requested before the activation slice is staged, so
+    // their latency overlaps the staging.
+    GroupRegs r0, r1, r2;
+    auto G = [&](int j) { return g0 + kWaves * j; };
+    if (n_my > 0) load_group<VEC>(p, rs, lo, G(0), r0);
+    stage_slice(p, rs, m0, mv, g_begin, g_end - g_begin, lds, row_e);
+    if (n_my > 1) load_group<VEC>(p, rs, lo, G(1), r1);
+
+    // Three register slots: while group j is computed, groups j+1 and j+2 are in flight.
+    // The steady-state loop issues only loads that exist; the last 1-4 groups are peeled.
+    if (n_my > 0) {
+        auto run = [&](const GroupRegs &r, int j) {
+            compute_group(r, lds + (wave + kWaves * j) * mv * kARowBytes, mv, lane, acc);
+        };
+        int j = 0;
+        for (; j + 4 < n_my; j += 3) {
+            load_group<VEC>(p, rs, lo, G(j + 2), r2);
+            run(r0, j);
+            load_group<VEC>(p, rs, lo, G(j + 3), r0);
+            run(r1, j + 1);
+            load_group<VEC>(p, rs, lo, G(j + 4), r1);
+            run(r2, j + 2);
         }
-        if (rd + 1 < rounds) {
-            const int gn = g + kWaves;
-            if (gn < g_end) load_group<VEC>(p, gn, n0, m0, mv, lane, ra);
-            char *buf = lds + ((rd + 1) & 1) * kLdsBufBytes + wave * kLdsWaveBytes;
-            int x = 0;
-            if (g < g_end) x = stage_activations(rb, buf, mv, lane);
-            __syncthreads();
-            if (g < g_end) compute_group(rb, buf, x, mv, lane, acc);
-            g = gn;
-        }
+        const int rem = n_my - j;  // 1..4 groups left; r0 (and r1) already loaded
+        if (rem >= 3) load_group<VEC>(p, rs, lo, G(j + 2), r2);
+        run(r0, j);
+        if (rem == 4) load_group<VEC>(p, rs, lo, G(j + 3), r0);
+        if (rem >= 2) run(r1, j + 1);
+        if (rem >= 3) run(r2, j + 2);
+        if (rem == 4) run(r0, j + 3);
+    }
+
+    // Undo the activation scale: output rows 4 kq + i were computed from A * 2^x[row].
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * kq + i;
+        const int x = 142 - row_e[row < kTileM ? row : 0];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t][i] = ldexpf(acc[t][i], -x);
     }
 
     // Reduce the 4 waves' accumulators through LDS (fixed order -> reproducible).
@@ -354,24 +426,37 @@ __global__ __launch_bounds__(kThreads) void w4a16_small_m_kernel(SmallParams p)
         return;
     }
 
+    // Split-K handoff.  Partials are written with device-coherent (write-through) stores
+    // and read back with device-coherent loads, so no L2 writeback or invalidate is
+    // needed: every thread waits for its stores to complete, the barrier orders that
+    // before thread 0 counts the arrival, and the workgroup that arrives last sums the
+    // partials in split order.
     float *tile_part = p.part + (int64_t)tile * p.splits * (kTileM * kTileN);
-    if (row < mv) *(f32x4 *)(tile_part + (int64_t)sp * (kTileM * kTileN) + row * kTileN + 4 * quad) = sum;
-    __threadfence();
+    if (row < mv) {
+        float *dst = tile_part + (int64_t)sp * (kTileM * kTileN) + row * kTileN + 4 * quad;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) __hip_atomic_store(dst + t, sum[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = atomicAdd(p.count + tile, 1u);
+        const unsigned prev = __hip_atomic_fetch_add(p.count + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (unsigned)(p.splits - 1));
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
+    asm volatile("" ::: "memory");
     if (row < mv) {
-        f32x4 tot = *(const f32x4 *)(tile_part + row * kTileN + 4 * quad);
-        for (int s = 1; s < p.splits; ++s)
-            tot += *(const f32x4 *)(tile_part + (int64_t)s * (kTileM * kTileN) + row * kTileN + 4 * quad);
+        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+        for (int sp2 = 0; sp2 < p.splits; ++sp2) {
+            const float *src = tile_part + (int64_t)sp2 * (kTileM * kTileN) + row * kTileN + 4 * quad;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                tot[t] += __hip_atomic_load(src + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         store_c(tot);
     }
-    if (threadIdx.x == 0) atomicExch(p.count + tile, 0u);
+    if (threadIdx.x == 0) __hip_atomic_store(p.count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(256) void w4_pack_kernel(const uint8_t *__restrict__ q,
@@ -446,42 +531,48 @@ w4_status check_device(int *dev_out)
 
 struct Workspace {
     char *ptr = nullptr;
-    size_t bytes = 0;
+    size_t counters = 0;     // capacity of the counter region, in counters
+    size_t part_bytes = 0;   // capacity of the partial region
 };
 std::map<std::pair<int, hipStream_t>, Workspace> g_workspaces;
 std::vector<char *> g_retired;  // superseded buffers stay valid for graphs captured earlier
 
-// Workspace layout: [counters, 256-byte aligned][partials]
-w4_status get_workspace(int dev, hipStream_t stream, size_t counter_bytes, size_t part_bytes,
+// Workspace layout, fixed for the life of a buffer: [counters][partials], the partial
+// region starting at counters * 4 rounded up to 256 bytes.  Counters are zero whenever no
+// call is in flight: the buffer is zeroed when allocated and every call resets the
+// counters it used.
+w4_status get_workspace(int dev, hipStream_t stream, size_t tiles, size_t part_bytes,
                         unsigned **count, float **part)
 {
-    const size_t cb = (counter_bytes + 255) & ~(size_t)255;
-    const size_t need = cb + part_bytes;
     std::lock_guard<std::mutex> lock(g_mutex);
     Workspace &ws = g_workspaces[{dev, stream}];
-    if (ws.bytes < need) {
+    if (ws.counters < tiles || ws.part_bytes < part_bytes) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         hipError_t e = hipStreamIsCapturing(stream, &cs);
         if (e != hipSuccess) return hip_fail("hipStreamIsCapturing", e);
         if (cs != hipStreamCaptureStatusNone) {
-            set_error("split-K workspace must grow to %zu bytes while the stream is capturing; "
-                      "run this shape once before capture", need);
+            set_error("split-K workspace must grow (%zu counters, %zu bytes) while the stream is "
+                      "capturing; run this shape once before capture", tiles, part_bytes);
             return W4_ERR_WORKSPACE;
         }
-        size_t bytes = need < ((size_t)1 << 20) ? ((size_t)1 << 20) : need;
-        bytes = (bytes + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
+        const size_t mib = (size_t)1 << 20;
+        size_t nc = ws.counters > tiles ? ws.counters : tiles;
+        nc = ((nc < 4096 ? 4096 : nc) + 1023) & ~(size_t)1023;
+        size_t pb = ws.part_bytes > part_bytes ? ws.part_bytes : part_bytes;
+        pb = ((pb < mib ? mib : pb) + mib - 1) & ~(mib - 1);
+        const size_t bytes = nc * 4 + pb;
         char *fresh = nullptr;
         e = hipMalloc((void **)&fresh, bytes);
         if (e != hipSuccess) return hip_fail("hipMalloc(workspace)", e);
-        // Counters must start at zero; every call leaves them at zero again.
         e = hipMemsetAsync(fresh, 0, bytes, stream);
         if (e != hipSuccess) return hip_fail("hipMemsetAsync(workspace)", e);
         if (ws.ptr) g_retired.push_back(ws.ptr);
         ws.ptr = fresh;
-        ws.bytes = bytes;
+        ws.counters = nc;
+        ws.part_bytes = pb;
     }
     *count = (unsigned *)ws.ptr;
-    *part = (float *)(ws.ptr + cb);
+    *part = (float *)(ws.ptr + ws.counters * 4);
     return W4_OK;
 }
 
@@ -489,6 +580,12 @@ w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N)
 {
     if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) {
         set_error("shape M=%lld K=%lld N=%lld: need M>=1, N>=1, K>=128, K%%128==0",
+                  (long long)M, (long long)K, (long long)N);
+        return W4_ERR_SHAPE;
+    }
+    // the kernels address each array with 32-bit byte offsets
+    if (K / 8 * N * 4 >= ((int64_t)1 << 31) || M * K * 2 >= ((int64_t)1 << 31)) {
+        set_error("shape M=%lld K=%lld N=%lld: packed weights or activations exceed 2 GiB",
                   (long long)M, (long long)K, (long long)N);
         return W4_ERR_SHAPE;
     }
@@ -505,11 +602,17 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     const int groups = (int)(K / kGroup);
     const int n_tiles = (int)((N + kTileN - 1) / kTileN);
     const int m_blocks = (int)((M + kTileM - 1) / kTileM);
+    const int rows = M < kTileM ? (int)M : kTileM;
     const int64_t base = (int64_t)n_tiles * m_blocks;
+    // enough workgroups to fill the GPU, at least one group per wave ...
     int splits = (int)((kTargetWorkgroups + base - 1) / base);
-    const int max_splits = groups / kWaves > 1 ? groups / kWaves : 1;  // >= 1 group per wave
+    const int max_splits = groups / kWaves > 1 ? groups / kWaves : 1;
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
+    // ... and an activation slice (rows x groups) that fits the LDS budget
+    const int max_gps = kMaxSliceRowGroups / rows;
+    const int min_splits = (groups + max_gps - 1) / max_gps;
+    if (splits < min_splits) splits = min_splits;
     const int gps = (groups + splits - 1) / splits;
     splits = (groups + gps - 1) / gps;
     pl->kernel = 1;
@@ -518,9 +621,14 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->splits = splits;
     pl->groups_per_split = gps;
     pl->workgroups = base * splits;
-    pl->workspace_bytes = splits > 1
-        ? (int64_t)((base * 4 + 255) & ~(int64_t)255) + base * splits * kTileM * kTileN * 4
-        : 0;
+    pl->workspace_bytes = splits > 1 ? base * 4 + base * splits * kTileM * kTileN * 4 : 0;
+}
+
+size_t slice_lds_bytes(int64_t M, const w4_plan &pl)
+{
+    const int rows = M < kTileM ? (int)M : kTileM;
+    const size_t slice = (size_t)rows * pl.groups_per_split * kARowBytes;
+    return slice > (size_t)kRedBytes ? slice : (size_t)kRedBytes;
 }
 
 }  // namespace
@@ -594,15 +702,16 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
     hipStream_t s = (hipStream_t)stream;
     if (pl.splits > 1) {
         const int64_t tiles = (int64_t)pl.n_tiles * pl.m_blocks;
-        st = get_workspace(dev, s, (size_t)tiles * 4,
-                           (size_t)tiles * pl.splits * kTileM * kTileN * 4, &p.count, &p.part);
+        st = get_workspace(dev, s, (size_t)tiles, (size_t)tiles * pl.splits * kTileM * kTileN * 4,
+                           &p.count, &p.part);
         if (st != W4_OK) return st;
     }
     const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros_u4, 4);
+    const size_t lds = slice_lds_bytes(M, pl);
     if (vec)
-        hipLaunchKernelGGL(w4a16_small_m_kernel<true>, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(w4a16_small_m_kernel<true>, dim3((unsigned)pl.workgroups), dim3(kThreads), lds, s, p);
     else
-        hipLaunchKernelGGL(w4a16_small_m_kernel<false>, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(w4a16_small_m_kernel<false>, dim3((unsigned)pl.workgroups), dim3(kThreads), lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("w4a16_gemm launch", e);
     return W4_OK;
