@@ -75,7 +75,7 @@ w4_status w4_pack(const uint8_t *q_u4, uint32_t *Wq, int64_t K, int64_t N, void 
 
 /* How w4a16_gemm would run a shape (host only, no HIP call). */
 typedef struct w4_plan {
-    int kernel;             /* 1 = small-M kernel (M-blocks of 16 rows)                     */
+    int kernel;             /* 1 = wide (4 waves per workgroup), 2 = tall (16 waves)        */
     int m_blocks;           /* row blocks of 16                                             */
     int n_tiles;            /* column tiles of 64                                           */
     int splits;             /* K splits across workgroups (1 = no workspace)                */

@@ -15,12 +15,12 @@
 //  * (q - z) is built in registers as exact binary16 pairs: a code is OR-ed into the
 //    mantissa of 1024.0 (or of 1024.0 + 16 q for the odd nibble of a byte) and the zero
 //    point is removed with one packed fp16 add/fma.  That is 9 VALU ops per 8 weights.
-//  * The products run on the matrix cores (v_mfma_f32_16x16x32_f16).  The activation tile
-//    is converted from bfloat16 to binary16 in LDS with a power-of-two scale per row and
-//    128-wide group, chosen so that row's largest magnitude in the group lands in
-//    [2^15, 2^16); the scale is undone exactly when the group's float32 partial is
-//    rescaled by s.  Every product a*(q-z) is then exact; bfloat16 values more than 2^29
-//    below the largest magnitude of their row within the group may be flushed (error
+//  * The products run on the matrix cores (v_mfma_f32_16x16x32_f16).  Each wave converts
+//    the activations of the group it is about to compute from bfloat16 to binary16 in its
+//    own LDS tile, row r scaled by 2^x[r] so that the row's largest magnitude in the group
+//    lands in [2^15, 2^16); the scale is undone exactly when the group's float32 partial
+//    is rescaled by s.  Every product a*(q-z) is then exact; bfloat16 values more than
+//    2^29 below the largest magnitude of their row within the group may be flushed (error
 //    below 2^-29 of that maximum per element).
 //  * Split-K across workgroups writes float32 partials to a workspace with device-coherent
 //    stores; a per-tile arrival counter elects the last workgroup, which sums the partials
@@ -50,18 +50,25 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;                  // waves per workgroup; each takes its own groups
-constexpr int kThreads = kWave * kWaves;
 constexpr int kTileN = 64;                 // output columns per workgroup (16 lanes x 4 words)
 constexpr int kTileM = 16;                 // output rows per M-block (one MFMA tile)
 constexpr int kGroup = 128;                // quantization group along K
 constexpr int kChunksPerRow = kGroup / 8;  // 16-byte activation chunks per group row
 constexpr int kARowBytes = (kChunksPerRow + 1) * 16;  // +16 bytes of padding: conflict-free reads
-constexpr int kMaxChunksPerThread = 12;     // activation slice <= 12 x 256 chunks (51 KiB of LDS)
-constexpr int kMaxSliceRowGroups = kMaxChunksPerThread * kThreads / kChunksPerRow;  // rows x groups
-constexpr int kRedBytes = kWaves * kTileM * kTileN * 4;
-constexpr int kTargetWorkgroups = 768;  // 256 CUs x 3 resident workgroups (3 waves per SIMD)
-constexpr int kCacheStream = 2;         // buffer-load cache policy: non-temporal (streamed once)
+constexpr int kCacheStream = 2;            // buffer-load cache policy: non-temporal (streamed once)
+constexpr int kCUs = 256;
+
+// Two shapes of the same kernel.  "Wide": 4 waves per workgroup, 3 workgroups resident per
+// CU, for outputs wide enough to fill the GPU with column tiles.  "Tall": 12 waves per
+// workgroup (one per CU) splitting K inside the workgroup, for narrow outputs, so that K is
+// reduced in LDS instead of across workgroups.  Both keep 3 waves per SIMD.
+struct Variant {
+    int waves;   // waves per workgroup
+    int per_cu;  // resident workgroups per CU
+};
+constexpr Variant kWide = {4, 3};
+constexpr Variant kTall = {12, 1};
+constexpr int kOccupancy = 3;  // waves per SIMD: at most 168 VGPRs per lane
 
 struct SmallParams {
     const uint16_t *A;
@@ -105,14 +112,12 @@ __device__ __forceinline__ f16x8 unpack8(uint32_t w, uint32_t zlo, uint32_t zhi,
 // Largest biased bfloat16 exponent among the 8 values of a chunk.
 __device__ __forceinline__ int chunk_max_exp(u32x4 v)
 {
-    int e = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t u = v[i];
-        int lo = (int)((u >> 7) & 0xFFu), hi = (int)((u >> 23) & 0xFFu);
-        e = max(e, max(lo, hi));
-    }
-    return e;
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t m = 0x7F807F80u;  // exponent fields of both halves
+    const u16x2 a = __builtin_elementwise_max(__builtin_bit_cast(u16x2, v[0] & m), __builtin_bit_cast(u16x2, v[1] & m));
+    const u16x2 b = __builtin_elementwise_max(__builtin_bit_cast(u16x2, v[2] & m), __builtin_bit_cast(u16x2, v[3] & m));
+    const u16x2 c = __builtin_elementwise_max(a, b);
+    return (int)(max(c.x, c.y) >> 7);
 }
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b)
@@ -227,10 +232,64 @@ __device__ __forceinline__ void load_group(const SmallParams &p, const Resources
     }
 }
 
-// One group of one wave: 4 MFMA steps per column subtile into the group partial P, then
-// acc += s * P (the activation tile is in LDS, scaled per row by 2^x).
-__device__ __forceinline__ void compute_group(const GroupRegs &r, const char *lds_group, int mv, int lane,
-                                              f32x4 (&acc)[4])
+
+// ------------------------------------------------------------------------------------
+// The GEMM kernel.  Each wave walks its own groups (every WAVES-th group of the
+// workgroup's K range).  For each group it converts that group's activations itself, with
+// one power-of-two scale per (row, group), right before computing it: the activation
+// chunks travel in the register ring with the group's weights, so the conversion overlaps
+// the loads still in flight and there is no workgroup-wide staging phase.
+
+template <int AV>
+struct PipeRegs {
+    u32x4 w[4];
+    u32x2 s;      // 4 binary16 scales
+    uint32_t z;   // 4 zero bytes
+    u32x4 a[AV];  // activation chunks: rows 4i + lane/16, chunk lane%16 of the group
+};
+
+constexpr int kPipeWaveBytes = kTileM * kARowBytes + kTileM * 4;  // tile + row exponents
+constexpr int kPipeExpOffset = kTileM * kARowBytes;
+
+template <bool VEC, int AV>
+__device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources &rs, const LaneOffsets<VEC> &o,
+                                          const uint32_t (&aoff)[AV], int g, PipeRegs<AV> &r)
+{
+    GroupRegs w;
+    load_group<VEC>(p, rs, o, g, w);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) r.w[st] = w.w[st];
+    r.s = w.s;
+    r.z = w.z;
+#pragma unroll
+    for (int i = 0; i < AV; ++i)
+        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[i], (uint32_t)g * (kGroup * 2), 0);
+}
+
+// Convert this wave's group of activations into its LDS tile: row r scaled by 2^x[r],
+// x[r] = 142 - (largest biased exponent of row r in the group); exponents stored next to
+// the tile.  The 16 chunks of a row sit in 16 consecutive lanes.
+template <int AV>
+__device__ __forceinline__ void stage_pipe(const PipeRegs<AV> &r, char *lds_wave, int mv, int lane)
+{
+    asm volatile("" ::: "memory");  // the previous group's LDS reads stay before these writes
+    const int kc = lane & 15;
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+        const int row = 4 * i + (lane >> 4);
+        int e = chunk_max_exp(r.a[i]);
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) e = max(e, __shfl_xor(e, off, 16));
+        const int x = 142 - max(e, 1);
+        if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = convert_chunk(r.a[i], x);
+        if (kc == 0) *(int *)(lds_wave + kPipeExpOffset + 4 * row) = row < mv ? x : 0;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's tile is complete
+}
+
+template <int AV>
+__device__ __forceinline__ void compute_pipe(const PipeRegs<AV> &r, const char *lds_wave, int mv, int lane,
+                                             f32x4 (&acc)[4])
 {
     const int c = lane & 15, kq = lane >> 4;
     uint32_t magic;
@@ -241,7 +300,6 @@ __device__ __forceinline__ void compute_group(const GroupRegs &r, const char *ld
         const uint32_t z = (r.z >> (8 * t)) & 0xFu;
         zlo[t] = (0xE400u | z) * 0x00010001u;         // -(1024 + z)
         zhi[t] = (0xD400u | (z << 4)) * 0x00010001u;  // -(64 + z)
-        // keep them in registers for the whole group instead of re-deriving per word
         asm volatile("" : "+v"(zlo[t]), "+v"(zhi[t]));
     }
     f32x4 P[4];
@@ -250,78 +308,29 @@ __device__ __forceinline__ void compute_group(const GroupRegs &r, const char *ld
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
         f16x8 a_op = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
-        if (c < mv) a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_group + c * kARowBytes + (4 * st + kq) * 16));
+        if (c < mv) a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_wave + c * kARowBytes + (4 * st + kq) * 16));
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const f16x8 b_op = unpack8(r.w[st][t], zlo[t], zhi[t], magic);
             P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, P[t], 0, 0, 0);
         }
     }
+    const int4 xr = *(const int4 *)(lds_wave + kPipeExpOffset + 16 * kq);
+    const int xs[4] = {xr.x, xr.y, xr.z, xr.w};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
         const float sv = (float)__builtin_bit_cast(_Float16, sb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(sv, P[t][i], acc[t][i]);
+        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(ldexpf(sv, -xs[i]), P[t][i], acc[t][i]);
     }
 }
 
-// Workgroup-wide barrier for LDS only: waits for this wave's LDS operations, not for its
-// global loads, so the weight loads already in flight stay in flight.
-__device__ __forceinline__ void lds_barrier()
+template <bool VEC, int WAVES, int AV, int OCC>
+__global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void w4a16_kernel(SmallParams p)
 {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Stage the workgroup's activation slice A[m0 .. m0+mv-1, 128 g_begin .. 128 g_end) into
-// LDS as binary16, row r scaled by 2^x[r] with x[r] = 142 - (largest biased exponent of
-// row r in the slice), which puts the row's largest magnitude in [2^15, 2^16).  Layout:
-// group gl, row r, chunk kc (8 values) at gl*mv*272 + r*272 + kc*16; 16 bytes of padding
-// per row keep the MFMA operand reads free of bank conflicts.  row_e ends up holding the
-// row exponents (0 for rows >= mv).
-__device__ __forceinline__ void stage_slice(const SmallParams &p, const Resources &rs, int m0, int mv,
-                                            int g_begin, int ng, char *lds_a, int *row_e)
-{
-    const int tid = threadIdx.x;
-    const int nch = mv * ng * kChunksPerRow;
-    u32x4 v[kMaxChunksPerThread];
-#pragma unroll
-    for (int i = 0; i < kMaxChunksPerThread; ++i) {
-        int ch = tid + kThreads * i;
-        ch = ch < nch ? ch : nch - 1;  // branch-free: spare threads reload the last chunk
-        const int kc = ch % kChunksPerRow, gr = ch / kChunksPerRow;
-        const int r = gr % mv, gl = gr / mv;
-        const uint32_t off = (uint32_t)(((int64_t)(m0 + r) * p.K + (int64_t)(g_begin + gl) * kGroup + kc * 8) * 2);
-        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, off, 0, 0);
-    }
-    if (tid < kTileM) row_e[tid] = 1;  // smallest normal exponent: all-zero rows stay at 2^0 scale
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < kMaxChunksPerThread; ++i) {
-        const int ch = tid + kThreads * i;
-        if (ch < nch) atomicMax(row_e + (ch / kChunksPerRow) % mv, chunk_max_exp(v[i]));
-    }
-    lds_barrier();
-#pragma unroll
-    for (int i = 0; i < kMaxChunksPerThread; ++i) {
-        const int ch = tid + kThreads * i;
-        if (ch < nch) {
-            const int gr = ch / kChunksPerRow;
-            const int x = 142 - row_e[gr % mv];
-            *(u32x4 *)(lds_a + gr * kARowBytes + (ch % kChunksPerRow) * 16) = convert_chunk(v[i], x);
-        }
-    }
-    lds_barrier();
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
-void w4a16_small_m_kernel(SmallParams p)
-{
-    extern __shared__ __attribute__((aligned(16))) char lds[];  // activation slice, then reduction
-    __shared__ int row_e[kTileM];
+    extern __shared__ __attribute__((aligned(16))) char lds[];  // per-wave tiles, then reduction
     __shared__ int s_last;
 
     const uint32_t logical = xcd_local_id(blockIdx.x, gridDim.x);
@@ -335,11 +344,11 @@ void w4a16_small_m_kernel(SmallParams p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
     const int c = lane & 15, kq = lane >> 4;
 
-    // This workgroup's groups are [g_begin, g_end); wave w takes g_begin + w, + 4, ...
     const int g_begin = sp * p.gps;
     const int g_end = min(p.groups, g_begin + p.gps);
     const int g0 = g_begin + wave;
-    const int n_my = g0 < g_end ? (g_end - g0 + kWaves - 1) / kWaves : 0;
+    const int n_my = g0 < g_end ? (g_end - g0 + WAVES - 1) / WAVES : 0;
+    char *tile_lds = lds + wave * kPipeWaveBytes;
 
     Resources rs;
     rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K / 8 * p.N * 4), kRsrcWord3);
@@ -348,69 +357,68 @@ void w4a16_small_m_kernel(SmallParams p)
     rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(p.M * p.K * 2), kRsrcWord3);
     LaneOffsets<VEC> lo;
     lane_offsets<VEC>(p, n0, lane, lo);
+    uint32_t aoff[AV];
+#pragma unroll
+    for (int i = 0; i < AV; ++i) {
+        int row = 4 * i + (lane >> 4);
+        row = row < mv ? row : mv - 1;
+        aoff[i] = (uint32_t)(((int64_t)(m0 + row) * p.K + (lane & 15) * 8) * 2);
+    }
+    // rows 4*AV..15 of this wave's exponent table are never staged: they read as 0
+    if (4 * AV < kTileM && lane >= 4 * AV && lane < kTileM) *(int *)(tile_lds + kPipeExpOffset + 4 * lane) = 0;
 
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // The first group's weights are requested before the activation slice is staged, so
-    // their latency overlaps the staging.
-    GroupRegs r0, r1, r2;
-    auto G = [&](int j) { return g0 + kWaves * j; };
-    if (n_my > 0) load_group<VEC>(p, rs, lo, G(0), r0);
-    stage_slice(p, rs, m0, mv, g_begin, g_end - g_begin, lds, row_e);
-    if (n_my > 1) load_group<VEC>(p, rs, lo, G(1), r1);
-
-    // Three register slots: while group j is computed, groups j+1 and j+2 are in flight.
-    // The steady-state loop issues only loads that exist; the last 1-4 groups are peeled.
+    // Two register slots: group j+1 (weights and activations) is in flight while group j is
+    // converted and computed.
+    auto G = [&](int j) { return g0 + WAVES * j; };
+    auto run = [&](const PipeRegs<AV> &r) {
+        stage_pipe<AV>(r, tile_lds, mv, lane);
+        compute_pipe<AV>(r, tile_lds, mv, lane, acc);
+    };
     if (n_my > 0) {
-        auto run = [&](const GroupRegs &r, int j) {
-            compute_group(r, lds + (wave + kWaves * j) * mv * kARowBytes, mv, lane, acc);
-        };
+        PipeRegs<AV> r0, r1;
+        load_pipe<VEC, AV>(p, rs, lo, aoff, G(0), r0);
         int j = 0;
-        for (; j + 4 < n_my; j += 3) {
-            load_group<VEC>(p, rs, lo, G(j + 2), r2);
-            run(r0, j);
-            load_group<VEC>(p, rs, lo, G(j + 3), r0);
-            run(r1, j + 1);
-            load_group<VEC>(p, rs, lo, G(j + 4), r1);
-            run(r2, j + 2);
+        for (; j + 2 < n_my; j += 2) {
+            load_pipe<VEC, AV>(p, rs, lo, aoff, G(j + 1), r1);
+            run(r0);
+            load_pipe<VEC, AV>(p, rs, lo, aoff, G(j + 2), r0);
+            run(r1);
         }
-        const int rem = n_my - j;  // 1..4 groups left; r0 (and r1) already loaded
-        if (rem >= 3) load_group<VEC>(p, rs, lo, G(j + 2), r2);
-        run(r0, j);
-        if (rem == 4) load_group<VEC>(p, rs, lo, G(j + 3), r0);
-        if (rem >= 2) run(r1, j + 1);
-        if (rem >= 3) run(r2, j + 2);
-        if (rem == 4) run(r0, j + 3);
+        if (j + 1 < n_my) {
+            load_pipe<VEC, AV>(p, rs, lo, aoff, G(j + 1), r1);
+            run(r0);
+            run(r1);
+        } else {
+            run(r0);
+        }
     }
 
-    // Undo the activation scale: output rows 4 kq + i were computed from A * 2^x[row].
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 4 * kq + i;
-        const int x = 142 - row_e[row < kTileM ? row : 0];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t][i] = ldexpf(acc[t][i], -x);
-    }
-
-    // Reduce the 4 waves' accumulators through LDS (fixed order -> reproducible).
+    // Reduce the waves' accumulators through LDS in wave order (reproducible).
     __syncthreads();
     float *red = (float *)lds;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        f32x4 v = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-        *(f32x4 *)(red + (wave * kTileM + 4 * kq + i) * kTileN + 4 * c) = v;
+        const int row = 4 * kq + i;
+        if (row < mv) {
+            f32x4 v = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+            *(f32x4 *)(red + (wave * mv + row) * kTileN + 4 * c) = v;
+        }
     }
     __syncthreads();
     const int row = threadIdx.x >> 4, quad = threadIdx.x & 15;
-    f32x4 sum = *(const f32x4 *)(red + (0 * kTileM + row) * kTileN + 4 * quad);
+    const bool valid = row < mv;
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+        sum = *(const f32x4 *)(red + row * kTileN + 4 * quad);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) sum += *(const f32x4 *)(red + (w * kTileM + row) * kTileN + 4 * quad);
-
+        for (int w = 1; w < WAVES; ++w) sum += *(const f32x4 *)(red + (w * mv + row) * kTileN + 4 * quad);
+    }
     const int64_t col = n0 + 4 * quad;
     auto store_c = [&](const f32x4 &v) {
-        if (row >= mv) return;
         float *dst = p.C + (int64_t)(m0 + row) * p.N + col;
         if (VEC) {
             if (col < p.N) *(f32x4 *)dst = v;
@@ -420,19 +428,12 @@ void w4a16_small_m_kernel(SmallParams p)
                 if (col + t < p.N) dst[t] = v[t];
         }
     };
-
     if (p.splits == 1) {
-        store_c(sum);
+        if (valid) store_c(sum);
         return;
     }
-
-    // Split-K handoff.  Partials are written with device-coherent (write-through) stores
-    // and read back with device-coherent loads, so no L2 writeback or invalidate is
-    // needed: every thread waits for its stores to complete, the barrier orders that
-    // before thread 0 counts the arrival, and the workgroup that arrives last sums the
-    // partials in split order.
     float *tile_part = p.part + (int64_t)tile * p.splits * (kTileM * kTileN);
-    if (row < mv) {
+    if (valid) {
         float *dst = tile_part + (int64_t)sp * (kTileM * kTileN) + row * kTileN + 4 * quad;
 #pragma unroll
         for (int t = 0; t < 4; ++t) __hip_atomic_store(dst + t, sum[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -446,13 +447,12 @@ void w4a16_small_m_kernel(SmallParams p)
     __syncthreads();
     if (!s_last) return;
     asm volatile("" ::: "memory");
-    if (row < mv) {
+    if (valid) {
         f32x4 tot = {0.f, 0.f, 0.f, 0.f};
         for (int sp2 = 0; sp2 < p.splits; ++sp2) {
             const float *src = tile_part + (int64_t)sp2 * (kTileM * kTileN) + row * kTileN + 4 * quad;
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                tot[t] += __hip_atomic_load(src + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int t = 0; t < 4; ++t) tot[t] += __hip_atomic_load(src + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         store_c(tot);
     }
@@ -597,25 +597,59 @@ w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N)
     return W4_OK;
 }
 
+// Launch plan.  Every workgroup of a launch should be resident at once (a second, partly
+// filled round would double the time); the rest is a small cost model in microseconds:
+//   launch + first-byte latency + max(streaming time, per-wave compute) + split-K handoff
+// where the streaming rate is limited by the bytes the resident waves keep in flight
+// (about one group each, over the loaded HBM latency) and by the achievable HBM rate.
+// Both kernel shapes and every split count are scored; the cheapest wins.
+constexpr double kUsLaunch = 3.5;        // dispatch + first bytes from HBM
+constexpr double kUsLatency = 1.6;       // loaded HBM latency seen by one wave
+constexpr double kGBsPeak = 6200.0;      // achievable streaming rate for this access pattern
+constexpr double kUsHandoff = 3.0;       // split-K: partial stores, arrival count, reload
+constexpr double kUsPerGroup = 0.55;     // one wave's compute for one group
+constexpr int kGroupBytes = 16 * 4 * kTileN;  // packed weights of one wave-group
+
+struct Choice {
+    const Variant *v;
+    int splits;
+    double us;
+};
+
+Choice score(const Variant &v, int64_t base, int groups, int splits)
+{
+    Choice c = {&v, splits, 1e30};
+    const int gps = (groups + splits - 1) / splits;
+    const int64_t wgs = base * splits;
+    if (wgs > (int64_t)v.per_cu * kCUs) return c;
+    const int per_wave = (gps + v.waves - 1) / v.waves;
+    const int active_waves_per_wg = gps < v.waves ? gps : v.waves;
+    const double inflight = (double)wgs * active_waves_per_wg * kGroupBytes;
+    double rate = inflight / (kUsLatency * 1e-6) / 1e9;  // GB/s
+    if (rate > kGBsPeak) rate = kGBsPeak;
+    const double bytes = (double)base * groups * kGroupBytes;
+    const double stream = bytes / (rate * 1e3);  // us
+    const double compute = per_wave * kUsPerGroup;
+    c.us = kUsLaunch + (stream > compute ? stream : compute) + (splits > 1 ? kUsHandoff : 0.0);
+    return c;
+}
+
 void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 {
     const int groups = (int)(K / kGroup);
     const int n_tiles = (int)((N + kTileN - 1) / kTileN);
     const int m_blocks = (int)((M + kTileM - 1) / kTileM);
-    const int rows = M < kTileM ? (int)M : kTileM;
     const int64_t base = (int64_t)n_tiles * m_blocks;
-    // enough workgroups to fill the GPU, at least one group per wave ...
-    int splits = (int)((kTargetWorkgroups + base - 1) / base);
-    const int max_splits = groups / kWaves > 1 ? groups / kWaves : 1;
-    if (splits > max_splits) splits = max_splits;
-    if (splits < 1) splits = 1;
-    // ... and an activation slice (rows x groups) that fits the LDS budget
-    const int max_gps = kMaxSliceRowGroups / rows;
-    const int min_splits = (groups + max_gps - 1) / max_gps;
-    if (splits < min_splits) splits = min_splits;
-    const int gps = (groups + splits - 1) / splits;
-    splits = (groups + gps - 1) / gps;
-    pl->kernel = 1;
+    Choice best = {&kWide, 1, 1e30};  // fallback (more tiles than resident slots): wide, no split
+    for (const Variant *v : {&kWide, &kTall}) {
+        for (int sp = 1; sp <= groups; ++sp) {
+            const Choice c = score(*v, base, groups, sp);
+            if (c.us < best.us) best = c;
+        }
+    }
+    const int gps = (groups + best.splits - 1) / best.splits;
+    const int splits = (groups + gps - 1) / gps;
+    pl->kernel = best.v == &kTall ? 2 : 1;
     pl->m_blocks = m_blocks;
     pl->n_tiles = n_tiles;
     pl->splits = splits;
@@ -624,11 +658,13 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->workspace_bytes = splits > 1 ? base * 4 + base * splits * kTileM * kTileN * 4 : 0;
 }
 
-size_t slice_lds_bytes(int64_t M, const w4_plan &pl)
+size_t plan_lds_bytes(int64_t M, const w4_plan &pl)
 {
     const int rows = M < kTileM ? (int)M : kTileM;
-    const size_t slice = (size_t)rows * pl.groups_per_split * kARowBytes;
-    return slice > (size_t)kRedBytes ? slice : (size_t)kRedBytes;
+    const Variant &v = pl.kernel == 2 ? kTall : kWide;
+    const size_t tiles = (size_t)v.waves * kPipeWaveBytes;
+    const size_t red = (size_t)v.waves * rows * kTileN * 4;
+    return tiles > red ? tiles : red;
 }
 
 }  // namespace
@@ -707,11 +743,19 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
         if (st != W4_OK) return st;
     }
     const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros_u4, 4);
-    const size_t lds = slice_lds_bytes(M, pl);
-    if (vec)
-        hipLaunchKernelGGL(w4a16_small_m_kernel<true>, dim3((unsigned)pl.workgroups), dim3(kThreads), lds, s, p);
-    else
-        hipLaunchKernelGGL(w4a16_small_m_kernel<false>, dim3((unsigned)pl.workgroups), dim3(kThreads), lds, s, p);
+    const size_t lds = plan_lds_bytes(M, pl);
+    const dim3 grid((unsigned)pl.workgroups);
+    const int rows = M < kTileM ? (int)M : kTileM;
+    const int av = (rows + 3) / 4;
+#define W4_LAUNCH(V, WV, AVV, OCCV) hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, OCCV>), grid, dim3(WV * kWave), lds, s, p)
+#define W4_LAUNCH_AV(V, WV, OCCV) \
+    switch (av) { case 1: W4_LAUNCH(V, WV, 1, OCCV); break; case 2: W4_LAUNCH(V, WV, 2, OCCV); break; \
+                  case 3: W4_LAUNCH(V, WV, 3, OCCV); break; default: W4_LAUNCH(V, WV, 4, OCCV); break; }
+    if (pl.kernel == 2) {
+        if (vec) { W4_LAUNCH_AV(true, 12, kOccupancy) } else { W4_LAUNCH_AV(false, 12, kOccupancy) }
+    } else {
+        if (vec) { W4_LAUNCH_AV(true, 4, kOccupancy) } else { W4_LAUNCH_AV(false, 4, kOccupancy) }
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("w4a16_gemm launch", e);
     return W4_OK;
