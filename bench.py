@@ -9,8 +9,9 @@ synchronization, timed with HIP events on the launch stream.
 
 Printed (one JSON line): effective weight GB/s (weight bytes = 4-bit codes + fp16 scales
 + u8 zeros per 128, i.e. 0.5234375 B per weight, divided by the step time), the fraction
-of the 8 TB/s HBM peak, the dominant kernel's roofline figures (per-launch durations from
-HIP events in a separate pass) and the oracle timed on the host cores on a bounded sample.
+of the 8 TB/s HBM peak, the dominant kernel's roofline figures (its average launch duration
+over the timed region, HBM traffic per launch from counters when a matching summary exists)
+and the oracle timed on the host cores on a bounded sample.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -20,17 +21,22 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
-MFMA_F16_PEAK_TFLOPS = 2500.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "W4A16 verify-GEMM effective weight GB/s and % of HBM roofline at M=gamma+1"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(ROOT, "int4_weight_only_gemm_amd", "csrc", "w4a16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_w4a16_small_m_kernel.json")
+KERNEL_NAME = "w4a16_kernel"
+# HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE passes (a text summary with
+# "key: value" lines); used only while the kernel source hash and workload still match.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_w4a16_kernel_qwen2.5-7b-verify-m5.md")
+CPU_SAMPLE_SECONDS = 10.0
 
 
 def log(msg):
@@ -42,6 +48,24 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def read_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel, or None when no summary matches."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            m = re.match(r"^\s*-?\s*`?([a-z0-9_]+)`?\s*:\s*`?([^`\s]+)`?\s*$", line)
+            if m:
+                kv[m.group(1)] = m.group(2)
+    if kv.get("kernel_source_sha256_16") != source_hash() or kv.get("workload") != workload:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -50,7 +74,6 @@ def parse():
     ap.add_argument("--workload", default="qwen2.5-7b-verify-m5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
-    ap.add_argument("--roofline-steps", type=int, default=3)
     ap.add_argument("--eager-steps", type=int, default=0,
                     help="only run this many eager steps (for a profiler) and print nothing else")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -100,7 +123,7 @@ def main():
             d["Wq"] = w4.pack(torch.from_numpy(x.q).to(dev))
         d["C"] = torch.empty((spec.M, spec.N), dtype=torch.float32, device=dev)
         gemms.append((spec, d))
-        if i < 4:
+        if not args.no_cpu_baseline:
             host_sample.append((spec, x))
     torch.cuda.synchronize()
     log(f"{args.workload}: {len(gemms)} GEMMs, {wl.weight_bytes / 1e9:.3f} GB of weights, "
@@ -165,62 +188,42 @@ def main():
     tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, {gbs:.1f} GB/s, {tflops:.2f} TFLOP/s")
 
-    # Roofline pass: per-launch HIP events on the launch stream. A GPU-side sleep first lets
-    # the host queue every launch, so each interval is the kernel's own execution.
-    n_launch = args.roofline_steps * len(calls)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
-    with torch.cuda.stream(stream):
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(int(2e8))
-        i = 0
-        for _ in range(args.roofline_steps):
-            for c in calls:
-                evs[i][0].record(stream)
-                rc = lib.w4a16_gemm(*c, handle)
-                if rc:
-                    raise w4.W4Error(rc, "w4a16_gemm")
-                evs[i][1].record(stream)
-                i += 1
-    torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) for a, b in evs]).reshape(args.roofline_steps, len(calls))
-    bytes_per_launch = np.array([spec.weight_bytes for spec, _ in gemms], dtype=np.float64)
-    flops_per_launch = np.array([spec.flops for spec, _ in gemms], dtype=np.float64)
-    avg_dur_ms = float(durs.mean())
+    # Roofline figures of the dominant kernel: every launch of a step is w4a16_gemm's kernel,
+    # so its average launch duration is the timed region (HIP events on the launch stream)
+    # divided by the launches it holds, and the algorithmic bytes (or flops) per launch are
+    # the step's totals divided by the same count.
+    launches = args.steps * len(calls)
+    avg_dur_s = elapsed_ms * 1e-3 / launches
     mfma_bound = max(spec.M for spec, _ in gemms) >= 64
-    if mfma_bound:  # batched verify: a dense contraction, priced against the fp16 MFMA peak
-        achieved = float(flops_per_launch.mean()) / (avg_dur_ms * 1e-3) / 1e12
-        peak, unit, bound = MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    if mfma_bound:  # batched verify: a dense contraction, priced against the bf16 MFMA peak
+        achieved = wl.flops / len(calls) / avg_dur_s / 1e12
+        peak, unit, bound = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     else:
-        achieved = float(bytes_per_launch.mean()) / (avg_dur_ms * 1e-3) / 1e9
+        achieved = wl.weight_bytes / len(calls) / avg_dur_s / 1e9
         peak, unit, bound = HBM_PEAK_GBS, "GB/s", "hbm"
-    per_shape = {}
-    for j, (spec, _) in enumerate(gemms):
-        key = f"{spec.M}x{spec.K}x{spec.N}"
-        per_shape.setdefault(key, []).append(durs[:, j].mean())
-    per_shape_us = {k: round(float(np.mean(v)) * 1e3, 3) for k, v in per_shape.items()}
-    log(f"dominant kernel: avg launch {avg_dur_ms * 1e3:.2f} us, {achieved:.1f} {unit}; per shape (us): {per_shape_us}")
+    log(f"dominant kernel: {launches} launches, avg {avg_dur_s * 1e6:.2f} us, {achieved:.1f} {unit}")
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("source_sha256_16") == source_hash() and tr.get("workload") == args.workload:
-            traffic = tr.get("hbm_bytes_per_launch")
+    traffic = read_traffic(args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:
+        # The oracle as it stands, on the host cores, over whole GEMMs of this workload taken
+        # in step order (wrapping round) until CPU_SAMPLE_SECONDS have passed.
         import oracle
         orc = oracle.get()
         threads = len(os.sched_getaffinity(0))
         t1 = time.perf_counter()
-        nbytes = 0
-        for spec, x in host_sample:
+        nbytes, done = 0, 0
+        while time.perf_counter() - t1 < CPU_SAMPLE_SECONDS:
+            spec, x = host_sample[done % len(host_sample)]
             Wq = x.Wq if x.Wq is not None else orc.pack(x.q)
             orc.gemm(x.A, Wq, x.S, x.Z, threads=threads)
             nbytes += spec.weight_bytes
+            done += 1
         dt = time.perf_counter() - t1
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-               "sample": f"{len(host_sample)} GEMMs (the first layer, every column) of {args.workload}, "
+               "sample": f"{done} GEMMs of {args.workload} in step order, wrapping round the step "
+                         f"({done / len(host_sample):.2f} steps of {len(host_sample)} GEMMs; every output element), "
                          f"{nbytes / 1e6:.1f} MB of weights in {dt:.2f} s"}
         log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads ({dt:.2f} s)")
 
@@ -235,7 +238,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tflops": round(tflops, 3),
@@ -248,14 +251,14 @@ def main():
         },
         "roofline": {
             "bound": bound,
-            "kernel": "w4a16_small_m_kernel",
+            "kernel": KERNEL_NAME,
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
-            "avg_launch_us": round(avg_dur_ms * 1e3, 3),
-            "per_shape_us": per_shape_us,
+            "avg_launch_us": round(avg_dur_s * 1e6, 3),
+            "launches_timed": launches,
         },
         "cpu_baseline": cpu,
     }
