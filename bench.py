@@ -32,7 +32,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "W4A16 verify-GEMM effective weight GB/s and % of HBM roofline at M=gamma+1"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(ROOT, "int4_weight_only_gemm_amd", "csrc", "w4a16.hip")
-KERNEL_NAME = "w4a16_kernel"
+KERNEL_NAME = "w4a16_kernel"           # small M: fp16 matrix cores, exact (q - z) operands
+KERNEL_NAME_LARGE = "w4a16_mfma_kernel"  # M >= 64: bf16 matrix cores
 # HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE passes (a text summary with
 # "key: value" lines); used only while the kernel source hash and workload still match.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_w4a16_kernel_qwen2.5-7b-verify-m5.md")
@@ -238,7 +239,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "bf16" if mfma_bound else "f16",
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tflops": round(tflops, 3),
@@ -251,7 +252,7 @@ def main():
         },
         "roofline": {
             "bound": bound,
-            "kernel": KERNEL_NAME,
+            "kernel": KERNEL_NAME_LARGE if mfma_bound else KERNEL_NAME,
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": unit,

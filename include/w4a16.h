@@ -22,6 +22,12 @@
  * Accuracy contract: every element satisfies
  *     |C - C_exact| <= 1e-4 * sum_k |A[m,k] * W[k,n]| + 1e-6.
  * The (q - z) factors and their products with A are exact; partial sums are float32.
+ * M >= 64 runs on the bfloat16 matrix cores with A used as given.  M < 64 runs on the
+ * binary16 matrix cores with A rescaled by a power of two per (row, 128-wide group), so
+ * that the group's largest |A| lands in [2^15, 2^16); elements more than 2^33 below that
+ * maximum are rounded to the binary16 subnormal grid (an absolute error below 2^-40 of
+ * the maximum per element, far inside the contract for any activation whose dynamic range
+ * within 128 consecutive values is under about 2^30).
  *
  * All entry points validate their arguments on the host before any HIP call and return a
  * status; launches are asynchronous on the given stream (NULL = the null stream), so device
@@ -75,9 +81,14 @@ w4_status w4_pack(const uint8_t *q_u4, uint32_t *Wq, int64_t K, int64_t N, void 
 
 /* How w4a16_gemm would run a shape (host only, no HIP call). */
 typedef struct w4_plan {
-    int kernel;             /* 1 = wide (4 waves per workgroup), 2 = tall (16 waves)        */
-    int m_blocks;           /* row blocks of 16                                             */
-    int n_tiles;            /* column tiles of 64                                           */
+    int kernel;             /* 1 = small-M wide (4 waves per workgroup, fp16 MFMA),
+                               2 = small-M tall (12 waves, fp16 MFMA),
+                               3 = large-M (M >= 64: 8 waves, bf16 MFMA)                  */
+    int tile_m;             /* output rows per row block (16 for kernels 1, 2; at most 160
+                               for kernel 3, computed in row tiles of 32)                    */
+    int tile_n;             /* output columns per workgroup tile (64, or 256 for kernel 3)   */
+    int m_blocks;           /* row blocks of tile_m                                          */
+    int n_tiles;            /* column tiles of tile_n                                        */
     int splits;             /* K splits across workgroups (1 = no workspace)                */
     int groups_per_split;   /* 128-wide K groups handled by one workgroup                   */
     int64_t workgroups;     /* grid size                                                     */

@@ -54,6 +54,8 @@ class W4Error(RuntimeError):
 class Plan(ctypes.Structure):
     _fields_ = [
         ("kernel", ctypes.c_int),
+        ("tile_m", ctypes.c_int),
+        ("tile_n", ctypes.c_int),
         ("m_blocks", ctypes.c_int),
         ("n_tiles", ctypes.c_int),
         ("splits", ctypes.c_int),

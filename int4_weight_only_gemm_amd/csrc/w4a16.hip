@@ -459,6 +459,296 @@ void w4a16_kernel(SmallParams p)
     if (threadIdx.x == 0) __hip_atomic_store(p.count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ------------------------------------------------------------------------------------
+// Large-M kernel (batched verify, M >= 64): a dense contraction on the bfloat16 matrix
+// cores (v_mfma_f32_32x32x16_bf16).  A workgroup owns a row block of up to RT*32 rows and
+// 256 columns; each of its 8 waves owns 32 columns, one per lane pair (lane l holds column
+// l % 32 and k-half l / 32 of every B operand), so every weight is loaded and dequantized
+// once per workgroup and reused by all RT row tiles.
+//
+// (q - z) is formed exactly in bfloat16: the codes of a word are biased into bytes
+// (0x80 | q) so that subtracting z cannot borrow across bytes, the bias is removed with
+// one xor, and each signed byte is converted int -> float -> bfloat16, all exact for
+// |q - z| <= 15.  Products on the matrix cores are then exact, and each group's float32
+// partial is rescaled by the fp16 scale once per output.
+//
+// Software pipeline per wave: weights are loaded two groups ahead; while group g's MFMAs
+// run, the next group's words are dequantized and the previous row tile's partials are
+// rescaled, so the VALU work interleaves with matrix-core work instead of forming a phase
+// of its own.  The activations of a group (rows x 128 bfloat16) are staged in LDS by the
+// whole workgroup, double-buffered, one barrier per group.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kLWaves = 8;
+constexpr int kLTileN = kLWaves * 32;  // 256 columns per workgroup
+constexpr int kLMaxRT = 5;             // up to 160 rows per workgroup (row tiles of 32)
+constexpr int kLThreads = kLWaves * kWave;
+
+struct LargeParams {
+    const uint16_t *A;
+    const uint32_t *Wq;
+    const uint16_t *S;
+    const uint8_t *Z;
+    float *C;
+    float *part;        // [m_blocks * n_tiles][splits][RT * 32][256] float32 partials
+    unsigned *count;    // [m_blocks * n_tiles] arrival counters, zero between calls
+    int64_t M, K, N;
+    int groups, splits, gps, n_tiles, m_blocks;
+    int block_rows;     // rows per row block (<= RT * 32)
+};
+
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b)
+{
+    bf16x2 h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Eight codes of one packed word -> eight exact bfloat16 values (q_j - z), j = 0..7 in k
+// order.  zz holds z in each of its four bytes.
+__device__ __forceinline__ bf16x8 unpack8_bf16(uint32_t w, uint32_t zz)
+{
+    const uint32_t ev = (((w & 0x0F0F0F0Fu) | 0x80808080u) - zz) ^ 0x80808080u;         // q0 q2 q4 q6
+    const uint32_t od = ((((w >> 4) & 0x0F0F0F0Fu) | 0x80808080u) - zz) ^ 0x80808080u;  // q1 q3 q5 q7
+    const float d0 = (float)(int8_t)ev, d2 = (float)(int8_t)(ev >> 8);
+    const float d4 = (float)(int8_t)(ev >> 16), d6 = (float)(int8_t)(ev >> 24);
+    const float d1 = (float)(int8_t)od, d3 = (float)(int8_t)(od >> 8);
+    const float d5 = (float)(int8_t)(od >> 16), d7 = (float)(int8_t)(od >> 24);
+    const u32x4 r = {pack_bf2(d0, d1), pack_bf2(d2, d3), pack_bf2(d4, d5), pack_bf2(d6, d7)};
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// One group's packed words for the lane's column: word ks holds k = 16 ks + 8 h .. + 7.
+struct LargeW {
+    uint32_t w[8];
+    uint32_t s;   // binary16 scale (low half)
+    uint32_t z;   // zero byte
+};
+
+template <int RT>
+__global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void w4a16_mfma_kernel(LargeParams p)
+{
+    constexpr int kRows = RT * 32;
+    constexpr int kBuf = kRows * kARowBytes;
+    constexpr int kAChunks = kRows * kChunksPerRow / kLThreads;  // == RT
+    static_assert(kRows * kChunksPerRow % kLThreads == 0, "staging must tile the block");
+    constexpr int kSteps = RT * 8;  // MFMAs per group per wave
+    __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
+    __shared__ int s_last;
+
+    const uint32_t logical = blockIdx.x;
+    const int sp = (int)(logical % (uint32_t)p.splits);
+    const uint32_t tile = logical / (uint32_t)p.splits;
+    const int nt = (int)(tile % (uint32_t)p.n_tiles);
+    const int mb = (int)(tile / (uint32_t)p.n_tiles);
+    const int64_t m0 = (int64_t)mb * p.block_rows;
+    const int64_t m_end = m0 + p.block_rows < p.M ? m0 + p.block_rows : p.M;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 31, h = lane >> 5;
+    const int64_t N = p.N;
+    const int64_t col = (int64_t)nt * kLTileN + wave * 32 + c;
+    const int64_t colc = col < N ? col : N - 1;
+
+    const int g_begin = sp * p.gps;
+    const int g_end = min(p.groups, g_begin + p.gps);
+
+    Resources rs;
+    rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K / 8 * N * 4), kRsrcWord3);
+    rs.S = __builtin_amdgcn_make_buffer_rsrc((void *)p.S, (short)0, (int)(p.K / kGroup * N * 2), kRsrcWord3);
+    rs.Z = __builtin_amdgcn_make_buffer_rsrc((void *)p.Z, (short)0, (int)(p.K / kGroup * N), kRsrcWord3);
+    rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(p.M * p.K * 2), kRsrcWord3);
+    const uint32_t woff = (uint32_t)((h * N + colc) * 4);
+    const uint32_t soff = (uint32_t)(colc * 2), zoff = (uint32_t)colc;
+    const uint32_t rowbytes = (uint32_t)N * 4;
+
+    // Activation staging: chunk id = thread + 512 j is (row id / 16, 16-byte chunk id % 16)
+    // of the group; rows outside the block read row m_end - 1 (never stored).
+    uint32_t aoff[kAChunks];
+    int alds[kAChunks];
+#pragma unroll
+    for (int j = 0; j < kAChunks; ++j) {
+        const int id = threadIdx.x + kLThreads * j;
+        const int row = id >> 4, kc = id & 15;
+        const int64_t srow = m0 + row < m_end ? m0 + row : m_end - 1;
+        aoff[j] = (uint32_t)((srow * p.K + kc * 8) * 2);
+        alds[j] = row * kARowBytes + kc * 16;
+    }
+    auto load_a = [&](int g, u32x4 (&ar)[kAChunks]) {
+#pragma unroll
+        for (int j = 0; j < kAChunks; ++j) ar[j] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[j], (uint32_t)g * (kGroup * 2), 0);
+    };
+    auto store_a = [&](int buf, const u32x4 (&ar)[kAChunks]) {
+#pragma unroll
+        for (int j = 0; j < kAChunks; ++j) *(u32x4 *)(lds + buf * kBuf + alds[j]) = ar[j];
+    };
+    auto load_w = [&](int g, LargeW &r) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            r.w[ks] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, woff, ((uint32_t)g * 16 + 2 * ks) * rowbytes, kCacheStream);
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs.S, soff, (uint32_t)g * (uint32_t)N * 2, 0);
+        r.z = __builtin_amdgcn_raw_buffer_load_b8(rs.Z, zoff, (uint32_t)g * (uint32_t)N, 0);
+    };
+    auto scale_of = [](const LargeW &r) { return (float)__builtin_bit_cast(_Float16, (uint16_t)r.s); };
+
+    f32x16 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[rt][v] = 0.f;
+
+    // A operand of (row tile rt, k-step ks): row rt*32 + c, k = 16 ks + 8 h .. + 7
+    const int a_lane = c * kARowBytes + h * 16;
+
+    // Two register sets for packed weights (X, Y) and two for dequantized operands (B0, B1)
+    // alternate between consecutive groups (the loop is unrolled by two), so no register
+    // set is ever copied: a copy would make the compiler wait for in-flight loads early.
+    u32x4 ar[kAChunks];
+    LargeW wx, wy;
+    bf16x8 B0[8], B1[8];
+    float sc0, sc1;
+
+    // One group: MFMAs on Bc (group g), dequantize Wn (group g + 1) into Bn, load group
+    // g + 2's weights into Wl and group g + 1's activations into ar.
+    auto group_step = [&](int g, LargeW &Wn, LargeW &Wl, const bf16x8 (&Bc)[8], bf16x8 (&Bn)[8],
+                          float sc, float &scn) {
+        const int buf = (g - g_begin) & 1;
+        const int gn1 = g + 1 < g_end ? g + 1 : g;  // clamped: the tail reloads, no branch
+        const int gn2 = g + 2 < g_end ? g + 2 : gn1;
+        load_a(gn1, ar);
+        load_w(gn2, Wl);
+        __builtin_amdgcn_sched_barrier(0);
+        // Pin this group's dequantization inside this group: without it the compiler may
+        // hoist it into the previous group, where it would wait for loads just issued.
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Wn.w[ks]));
+        asm volatile("" : "+v"(Wn.z), "+v"(Wn.s));
+
+        const char *abase = lds + buf * kBuf + a_lane;
+        const uint32_t zzn = (Wn.z & 0xFu) * 0x01010101u;
+        constexpr int kAhead = 2;  // A operands read two steps ahead (step = rt * 8 + ks)
+        bf16x8 ring[kAhead + 1];
+        auto a_at = [&](int step) { return *(const bf16x8 *)(abase + (step >> 3) * 32 * kARowBytes + (step & 7) * 32); };
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) ring[i] = a_at(i);
+        // Step (rt, ks): read the A operand two steps ahead, issue the MFMA, then a share
+        // of the VALU work: dequantize one word every RT steps, and rescale two of row tile
+        // rt - 1's sixteen partials (their MFMAs finished a row tile ago).  A scheduling
+        // barrier after each step keeps this order.
+        f32x16 P, Q;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int step = rt * 8 + ks;
+                if (step + kAhead < kSteps) ring[(step + kAhead) % (kAhead + 1)] = a_at(step + kAhead);
+                const bf16x8 a = ring[step % (kAhead + 1)];
+                if (ks == 0) {
+                    const f32x16 zero = {};
+                    P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], zero, 0, 0, 0);
+                } else {
+                    P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], P, 0, 0, 0);
+                }
+                if (step % RT == 0) Bn[step / RT] = unpack8_bf16(Wn.w[step / RT], zzn);
+                if (rt > 0) {
+                    acc[rt - 1][2 * ks] = __builtin_fmaf(sc, Q[2 * ks], acc[rt - 1][2 * ks]);
+                    acc[rt - 1][2 * ks + 1] = __builtin_fmaf(sc, Q[2 * ks + 1], acc[rt - 1][2 * ks + 1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            Q = P;
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[RT - 1][v] = __builtin_fmaf(sc, Q[v], acc[RT - 1][v]);
+        scn = scale_of(Wn);
+        // ... and keep it from sinking into the next group: the operands are complete here.
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Bn[ks]));
+        store_a(buf ^ 1, ar);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    load_a(g_begin, ar);
+    load_w(g_begin, wy);
+    load_w(g_begin + 1 < g_end ? g_begin + 1 : g_begin, wx);
+    {
+        const uint32_t zz = (wy.z & 0xFu) * 0x01010101u;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) B0[ks] = unpack8_bf16(wy.w[ks], zz);
+        sc0 = scale_of(wy);
+    }
+    store_a(0, ar);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    for (int g = g_begin; g < g_end; g += 2) {
+        group_step(g, wx, wy, B0, B1, sc0, sc1);
+        if (g + 1 >= g_end) break;
+        group_step(g + 1, wy, wx, B1, B0, sc1, sc0);
+    }
+
+    // Lane holds column col and rows rt*32 + 8 (v / 4) + 4 h + v % 4 of the block.
+    auto out_row = [&](int rt, int v) { return rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3); };
+    if (p.splits == 1) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + out_row(rt, v);
+                if (row < m_end && col < N) p.C[row * N + col] = acc[rt][v];
+            }
+        return;
+    }
+    // Split-K: device-coherent partial stores, arrival count, and the last workgroup of the
+    // tile sums the partials in split order and writes C.
+    const int lcol = wave * 32 + c;
+    float *tile_part = p.part + (int64_t)tile * p.splits * (kRows * kLTileN);
+    {
+        float *dst = tile_part + (int64_t)sp * (kRows * kLTileN) + lcol;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                __hip_atomic_store(dst + out_row(rt, v) * kLTileN, acc[rt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(p.count + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == (unsigned)(p.splits - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[rt][v] = 0.f;
+    for (int s2 = 0; s2 < p.splits; ++s2) {
+        const float *src = tile_part + (int64_t)s2 * (kRows * kLTileN) + lcol;
+        float t[RT][16];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                t[rt][v] = __hip_atomic_load(src + out_row(rt, v) * kLTileN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[rt][v] += t[rt][v];
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int64_t row = m0 + out_row(rt, v);
+            if (row < m_end && col < N) p.C[row * N + col] = acc[rt][v];
+        }
+    if (threadIdx.x == 0) __hip_atomic_store(p.count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ __launch_bounds__(256) void w4_pack_kernel(const uint8_t *__restrict__ q,
                                                       uint32_t *__restrict__ Wq, int64_t KB, int64_t N)
 {
@@ -634,7 +924,72 @@ Choice score(const Variant &v, int64_t base, int groups, int splits)
     return c;
 }
 
-void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
+// Large-M plan.  Candidates: row blocks of up to 160 rows (each weight dequantized once)
+// or more, smaller row blocks (more tiles for narrow outputs, each weight dequantized once
+// per block), times every K split.  The score is a small cost model in microseconds:
+//   rounds of resident workgroups x groups per split x time per group
+//   + split-K handoff (partial stores, arrival count, the last workgroup reading every
+//     split's partial tile back)
+// where the time per group is the larger of the matrix-core time and the VALU time
+// (dequantization, rescale and MFMA issue) of one workgroup, at a sustained efficiency.
+constexpr double kLargeClockGHz = 2.4;
+constexpr double kLargeEff = 0.8;          // sustained fraction of the issue-limited rate
+constexpr double kUsLargeHandoff = 2.0;    // partial stores, arrival count
+constexpr double kLargeReadGBs = 150.0;    // one workgroup reading partial tiles back
+constexpr int kLargeMinM = 64;
+
+bool large_path(int64_t M, int64_t /*N*/) { return M >= kLargeMinM; }
+
+double large_group_us(int rt)
+{
+    const double mfma = 2.0 * rt * 8 * 32;                     // cycles per SIMD, 2 waves
+    const double valu = 2.0 * (160 + 16 * rt + 8 * rt) * 4;   // unpack + rescale + MFMA issue
+    return (mfma > valu ? mfma : valu) / (kLargeClockGHz * 1e3) / kLargeEff;
+}
+
+void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
+{
+    const int groups = (int)(K / kGroup);
+    const int n_tiles = (int)((N + kLTileN - 1) / kLTileN);
+    const int min_blocks = (int)((M + kLMaxRT * 32 - 1) / (kLMaxRT * 32));
+    double best_us = 1e30;
+    int best_mb = min_blocks, best_s = 1, best_rows = 0, best_rt = kLMaxRT;
+    for (int mbk = min_blocks; mbk <= 2 * min_blocks; ++mbk) {
+        const int rows = (int)((M + mbk - 1) / mbk);
+        const int rt = (rows + 31) / 32;
+        if (rt < 2 || (int64_t)(mbk - 1) * rows >= M) continue;
+        const int64_t base = (int64_t)mbk * n_tiles;
+        const double tg = large_group_us(rt);
+        const double part_us = (double)rt * 32 * kLTileN * 4 / (kLargeReadGBs * 1e3);
+        for (int sp = 1; sp <= groups; ++sp) {
+            const int gps = (groups + sp - 1) / sp;
+            if ((groups + gps - 1) / gps != sp) continue;
+            const int64_t rounds = (base * sp + kCUs - 1) / kCUs;
+            double us = (double)rounds * gps * tg;
+            if (sp > 1) us += kUsLargeHandoff + sp * part_us;
+            if (us < best_us) {
+                best_us = us;
+                best_mb = mbk;
+                best_s = sp;
+                best_rows = rows;
+                best_rt = rt;
+            }
+        }
+    }
+    const int gps = (groups + best_s - 1) / best_s;
+    const int64_t base = (int64_t)best_mb * n_tiles;
+    pl->kernel = 3;
+    pl->tile_m = best_rows;
+    pl->tile_n = kLTileN;
+    pl->m_blocks = best_mb;
+    pl->n_tiles = n_tiles;
+    pl->splits = best_s;
+    pl->groups_per_split = gps;
+    pl->workgroups = base * best_s;
+    pl->workspace_bytes = best_s > 1 ? base * 4 + base * best_s * (int64_t)best_rt * 32 * kLTileN * 4 : 0;
+}
+
+void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 {
     const int groups = (int)(K / kGroup);
     const int n_tiles = (int)((N + kTileN - 1) / kTileN);
@@ -650,12 +1005,24 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     const int gps = (groups + best.splits - 1) / best.splits;
     const int splits = (groups + gps - 1) / gps;
     pl->kernel = best.v == &kTall ? 2 : 1;
+    pl->tile_m = kTileM;
+    pl->tile_n = kTileN;
     pl->m_blocks = m_blocks;
     pl->n_tiles = n_tiles;
     pl->splits = splits;
     pl->groups_per_split = gps;
     pl->workgroups = base * splits;
     pl->workspace_bytes = splits > 1 ? base * 4 + base * splits * kTileM * kTileN * 4 : 0;
+}
+
+// M >= 64 with N even runs on the bf16 matrix-core kernel; everything else on the
+// small-M kernel (row blocks of 16).
+void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
+{
+    if (large_path(M, N))
+        make_large_plan(M, K, N, pl);
+    else
+        make_small_plan(M, K, N, pl);
 }
 
 size_t plan_lds_bytes(int64_t M, const w4_plan &pl)
@@ -719,42 +1086,73 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
 
     w4_plan pl;
     make_plan(M, K, N, &pl);
-    SmallParams p;
-    p.A = (const uint16_t *)A_bf16;
-    p.Wq = Wq;
-    p.S = (const uint16_t *)scales_f16;
-    p.Z = zeros_u4;
-    p.C = C;
-    p.part = nullptr;
-    p.count = nullptr;
-    p.M = M;
-    p.K = K;
-    p.N = N;
-    p.groups = (int)(K / kGroup);
-    p.splits = pl.splits;
-    p.gps = pl.groups_per_split;
-    p.n_tiles = pl.n_tiles;
-    p.m_blocks = pl.m_blocks;
     hipStream_t s = (hipStream_t)stream;
+    unsigned *count = nullptr;
+    float *part = nullptr;
     if (pl.splits > 1) {
         const int64_t tiles = (int64_t)pl.n_tiles * pl.m_blocks;
-        st = get_workspace(dev, s, (size_t)tiles, (size_t)tiles * pl.splits * kTileM * kTileN * 4,
-                           &p.count, &p.part);
+        st = get_workspace(dev, s, (size_t)tiles, (size_t)(pl.workspace_bytes - tiles * 4), &count, &part);
         if (st != W4_OK) return st;
     }
-    const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros_u4, 4);
-    const size_t lds = plan_lds_bytes(M, pl);
     const dim3 grid((unsigned)pl.workgroups);
-    const int rows = M < kTileM ? (int)M : kTileM;
-    const int av = (rows + 3) / 4;
+    if (pl.kernel == 3) {
+        LargeParams q;
+        q.A = (const uint16_t *)A_bf16;
+        q.Wq = Wq;
+        q.S = (const uint16_t *)scales_f16;
+        q.Z = zeros_u4;
+        q.C = C;
+        q.part = part;
+        q.count = count;
+        q.M = M;
+        q.K = K;
+        q.N = N;
+        q.groups = (int)(K / kGroup);
+        q.splits = pl.splits;
+        q.gps = pl.groups_per_split;
+        q.n_tiles = pl.n_tiles;
+        q.m_blocks = pl.m_blocks;
+        q.block_rows = pl.tile_m;
+#define W4_LAUNCH_L(RTV) hipLaunchKernelGGL((w4a16_mfma_kernel<RTV>), grid, dim3(kLThreads), 0, s, q)
+        switch ((pl.tile_m + 31) / 32) {
+        case 2: W4_LAUNCH_L(2); break;
+        case 3: W4_LAUNCH_L(3); break;
+        case 4: W4_LAUNCH_L(4); break;
+        default: W4_LAUNCH_L(5); break;
+        }
+#undef W4_LAUNCH_L
+    } else {
+        SmallParams p;
+        p.A = (const uint16_t *)A_bf16;
+        p.Wq = Wq;
+        p.S = (const uint16_t *)scales_f16;
+        p.Z = zeros_u4;
+        p.C = C;
+        p.part = part;
+        p.count = count;
+        p.M = M;
+        p.K = K;
+        p.N = N;
+        p.groups = (int)(K / kGroup);
+        p.splits = pl.splits;
+        p.gps = pl.groups_per_split;
+        p.n_tiles = pl.n_tiles;
+        p.m_blocks = pl.m_blocks;
+        const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros_u4, 4);
+        const size_t lds = plan_lds_bytes(M, pl);
+        const int rows = M < kTileM ? (int)M : kTileM;
+        const int av = (rows + 3) / 4;
 #define W4_LAUNCH(V, WV, AVV, OCCV) hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, OCCV>), grid, dim3(WV * kWave), lds, s, p)
 #define W4_LAUNCH_AV(V, WV, OCCV) \
     switch (av) { case 1: W4_LAUNCH(V, WV, 1, OCCV); break; case 2: W4_LAUNCH(V, WV, 2, OCCV); break; \
                   case 3: W4_LAUNCH(V, WV, 3, OCCV); break; default: W4_LAUNCH(V, WV, 4, OCCV); break; }
-    if (pl.kernel == 2) {
-        if (vec) { W4_LAUNCH_AV(true, 12, kOccupancy) } else { W4_LAUNCH_AV(false, 12, kOccupancy) }
-    } else {
-        if (vec) { W4_LAUNCH_AV(true, 4, kOccupancy) } else { W4_LAUNCH_AV(false, 4, kOccupancy) }
+        if (pl.kernel == 2) {
+            if (vec) { W4_LAUNCH_AV(true, 12, kOccupancy) } else { W4_LAUNCH_AV(false, 12, kOccupancy) }
+        } else {
+            if (vec) { W4_LAUNCH_AV(true, 4, kOccupancy) } else { W4_LAUNCH_AV(false, 4, kOccupancy) }
+        }
+#undef W4_LAUNCH_AV
+#undef W4_LAUNCH
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("w4a16_gemm launch", e);

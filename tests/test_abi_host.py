@@ -76,8 +76,13 @@ def test_plan_covers_shapes():
             seen.add(key)
             p = w4.plan(*key)
             groups = g.K // 128
-            assert p["n_tiles"] * 64 >= g.N > (p["n_tiles"] - 1) * 64
-            assert p["m_blocks"] * 16 >= g.M > (p["m_blocks"] - 1) * 16
+            assert (p["kernel"] == 3) == (g.M >= 64)
+            if p["kernel"] == 3:
+                assert p["tile_n"] == 256 and p["tile_m"] <= 160
+            else:
+                assert (p["tile_m"], p["tile_n"]) == (16, 64)
+            assert p["n_tiles"] * p["tile_n"] >= g.N > (p["n_tiles"] - 1) * p["tile_n"]
+            assert p["m_blocks"] * p["tile_m"] >= g.M > (p["m_blocks"] - 1) * p["tile_m"]
             assert p["splits"] * p["groups_per_split"] >= groups
             assert (p["splits"] - 1) * p["groups_per_split"] < groups
             assert p["workgroups"] == p["n_tiles"] * p["m_blocks"] * p["splits"]

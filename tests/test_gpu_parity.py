@@ -279,3 +279,122 @@ def test_workload_gamma_sweep_sampled(orc):
     for M in (3, 4, 5, 6, 7):
         for spec in [g for g in wl.gemms if g.M == M][:2]:
             _sampled_check(orc, spec, ncols=24)
+
+
+# ------------------------------------------------------ large M (bf16 matrix-core kernel)
+LARGE_SHAPES = [(128, 2), (256, 256), (384, 258), (1152, 520)]
+
+
+@pytest.mark.parametrize("M", [64, 96, 100, 160, 161, 250, 320])
+def test_large_m_grid(orc, M):
+    worst = 0.0
+    for K, N in LARGE_SHAPES:
+        p = w4.plan(M, K, N)
+        assert p["kernel"] == 3
+        log(f"large grid M={M} K={K} N={N} plan={p}")
+        x = synth.generate_custom(M, K, N, seed=21)
+        C = run(to_dev(x)).cpu().numpy()
+        Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
+        worst = max(worst, check(C, Cr, Cabs, f"large M={M} K={K} N={N}"))
+    log(f"large grid M={M}: worst error / bound = {worst:.3g}")
+
+
+@pytest.mark.parametrize("M,K,N", [(160, 4096, 4096), (160, 11008, 4096), (64, 8192, 512), (200, 2048, 1030),
+                                   (160, 4096, 12288)])
+def test_large_m_split_k(orc, M, K, N):
+    p = w4.plan(M, K, N)
+    log(f"large split-K M={M} K={K} N={N} plan={p}")
+    x = synth.generate_custom(M, K, N, seed=22)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    C = run(to_dev(x), out=out).cpu().numpy()
+    assert np.all(np.isfinite(C))
+    cols = np.unique(np.r_[0, 1, N - 2, N - 1, np.random.default_rng(23).integers(0, N, 40)])
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+    check(C[:, cols], Cr, Cabs, f"large split M={M} K={K} N={N}")
+
+
+def test_large_m_one_hot_bitwise(orc):
+    M, K, N = 160, 384, 256
+    x = synth.generate_custom(M, K, N, seed=24)
+    dev = to_dev(x)
+    for (m0, k0, a0) in ((0, 0, 1.0), (M - 1, K - 1, -2.5), (77, 131, 3.0e4), (150, 200, -0.0078125)):
+        A = np.zeros((M, K), np.float32)
+        A[m0, k0] = a0
+        dev["A"] = torch.from_numpy(synth.f32_to_bf16_bits(A).view(np.int16)).cuda().view(torch.bfloat16)
+        log(f"large one-hot m={m0} k={k0} a={a0}")
+        C = run(dev).cpu().numpy()
+        Cr, _ = orc.gemm(synth.f32_to_bf16_bits(A), x.Wq, x.S, x.Z)
+        assert np.array_equal(C, Cr.astype(np.float32)), "one-hot row differs"
+
+
+def test_large_m_zero_and_identity(orc):
+    M, K, N = 160, 1152, 258
+    x = synth.generate_custom(M, K, N, seed=25)
+    q = np.repeat(x.Z, 128, axis=0).astype(np.uint8)
+    log("large zero case q == z")
+    C = run(to_dev(synth.GemmInputs(A=x.A, Wq=orc.pack(q), q=None, S=x.S, Z=x.Z))).cpu().numpy()
+    assert np.all(C == 0.0)
+    Z = np.random.default_rng(26).integers(0, 15, size=x.Z.shape, dtype=np.uint8)
+    q = np.repeat(Z + 1, 128, axis=0).astype(np.uint8)
+    S = np.ones(x.S.shape, np.float16).view(np.uint16)
+    xi = synth.GemmInputs(A=x.A, Wq=orc.pack(q), q=None, S=S, Z=Z)
+    log("large identity q = z + 1, s = 1")
+    C = run(to_dev(xi)).cpu().numpy()
+    Cr, Cabs = orc.gemm(xi.A, xi.Wq, xi.S, xi.Z)
+    check(C, Cr, Cabs, "large identity")
+    assert np.all(C == C[:, :1])
+
+
+def test_large_m_dynamic_range(orc):
+    M, K, N = 64, 512, 64
+    x = synth.generate_custom(M, K, N, seed=27)
+    a = (x.A.astype(np.uint32) << 16).view(np.float32)
+    scale = np.geomspace(1e30, 1e-30, M).astype(np.float32)[:, None]
+    A = synth.f32_to_bf16_bits(a * scale)
+    xs = synth.GemmInputs(A=A, Wq=x.Wq, q=None, S=x.S, Z=x.Z)
+    log("large activation dynamic range")
+    C = run(to_dev(xs)).cpu().numpy()
+    Cr, Cabs = orc.gemm(xs.A, xs.Wq, xs.S, xs.Z)
+    check(C, Cr, Cabs, "large dynamic range")
+
+
+def test_large_m_unaligned_views_fall_back(orc):
+    # 2-byte aligned scales take the small-M kernel for M >= 64; results stay in tolerance
+    M, K, N = 96, 512, 128
+    x = synth.generate_custom(M, K, N, seed=28)
+    dev = to_dev(x)
+    G = K // 128
+    s_big = torch.empty(G * N + 1, dtype=torch.float16, device="cuda")
+    s_big[1:] = dev["S"].flatten()
+    dev["S"] = s_big[1:].view(G, N)
+    log("large unaligned scale view")
+    C = run(dev).cpu().numpy()
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
+    check(C, Cr, Cabs, "large unaligned")
+
+
+def test_large_m_graph_and_reproducible():
+    shapes = [(160, 4096, 4096), (160, 4096, 22016), (160, 11008, 4096)]
+    xs = [to_dev(synth.generate_custom(M, K, N, seed=29)) for (M, K, N) in shapes]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        eager = [run(d).clone() for d in xs]
+        again = [run(d).clone() for d in xs]
+    torch.cuda.synchronize()
+    for e, a in zip(eager, again):
+        assert torch.equal(e, a), "large split-K result not reproducible"
+    outs = [torch.empty_like(e) for e in eager]
+    g = torch.cuda.CUDAGraph()
+    log("large graph capture")
+    with torch.cuda.graph(g, stream=s):
+        for d, o in zip(xs, outs):
+            run(d, out=o)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        log(f"large graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for e, o in zip(eager, outs):
+            assert torch.equal(e, o), f"replay {rep} differs from eager"
