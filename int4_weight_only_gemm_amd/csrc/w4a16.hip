@@ -31,6 +31,7 @@
 
 #include <cstdarg>
 #include <cstdint>
+#include <type_traits>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -493,8 +494,8 @@ struct LargeParams {
     const uint16_t *S;
     const uint8_t *Z;
     float *C;
-    float *part;        // [m_blocks * n_tiles][splits][RT * 32][256] float32 partials
-    unsigned *count;    // [m_blocks * n_tiles] arrival counters, zero between calls
+    float *part;        // [splits][stride] float32 partial products (split-K only)
+    int64_t stride;     // floats per split slice: M * N rounded up to a multiple of 4
     int64_t M, K, N;
     int groups, splits, gps, n_tiles, m_blocks;
     int block_rows;     // rows per row block (<= RT * 32)
@@ -533,11 +534,10 @@ void w4a16_mfma_kernel(LargeParams p)
 {
     constexpr int kRows = RT * 32;
     constexpr int kBuf = kRows * kARowBytes;
-    constexpr int kAChunks = kRows * kChunksPerRow / kLThreads;  // == RT
+    constexpr int kAChunks = kRows * kChunksPerRow / kLThreads;  // == RT: one per row tile
     static_assert(kRows * kChunksPerRow % kLThreads == 0, "staging must tile the block");
     constexpr int kSteps = RT * 8;  // MFMAs per group per wave
     __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
-    __shared__ int s_last;
 
     const uint32_t logical = blockIdx.x;
     const int sp = (int)(logical % (uint32_t)p.splits);
@@ -660,6 +660,9 @@ void w4a16_mfma_kernel(LargeParams p)
                 __builtin_amdgcn_sched_barrier(0);
             }
             Q = P;
+            // stage one chunk of the next group's activations per row tile, so the LDS
+            // writes spread over the group instead of queueing behind its reads at the end
+            *(u32x4 *)(lds + (buf ^ 1) * kBuf + alds[rt]) = ar[rt];
         }
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[RT - 1][v] = __builtin_fmaf(sc, Q[v], acc[RT - 1][v]);
@@ -667,7 +670,6 @@ void w4a16_mfma_kernel(LargeParams p)
         // ... and keep it from sinking into the next group: the operands are complete here.
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Bn[ks]));
-        store_a(buf ^ 1, ar);
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -689,64 +691,38 @@ void w4a16_mfma_kernel(LargeParams p)
         group_step(g + 1, wy, wx, B1, B0, sc1, sc0);
     }
 
-    // Lane holds column col and rows rt*32 + 8 (v / 4) + 4 h + v % 4 of the block.
-    auto out_row = [&](int rt, int v) { return rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3); };
-    if (p.splits == 1) {
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + out_row(rt, v);
-                if (row < m_end && col < N) p.C[row * N + col] = acc[rt][v];
-            }
-        return;
-    }
-    // Split-K: device-coherent partial stores, arrival count, and the last workgroup of the
-    // tile sums the partials in split order and writes C.
-    const int lcol = wave * 32 + c;
-    float *tile_part = p.part + (int64_t)tile * p.splits * (kRows * kLTileN);
-    {
-        float *dst = tile_part + (int64_t)sp * (kRows * kLTileN) + lcol;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                __hip_atomic_store(dst + out_row(rt, v) * kLTileN, acc[rt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(p.count + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (unsigned)(p.splits - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[rt][v] = 0.f;
-    for (int s2 = 0; s2 < p.splits; ++s2) {
-        const float *src = tile_part + (int64_t)s2 * (kRows * kLTileN) + lcol;
-        float t[RT][16];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                t[rt][v] = __hip_atomic_load(src + out_row(rt, v) * kLTileN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[rt][v] += t[rt][v];
-    }
+    // Lane holds column col and rows rt*32 + 8 (v / 4) + 4 h + v % 4 of the block.  Without
+    // a K split the results go to C; with one, each split writes its partial product to its
+    // own [M, N] slice and w4a16_split_reduce adds the slices in split order (the kernel
+    // boundary orders the two).
+    float *out = p.splits == 1 ? p.C : p.part + (int64_t)sp * p.stride;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int64_t row = m0 + out_row(rt, v);
-            if (row < m_end && col < N) p.C[row * N + col] = acc[rt][v];
+            const int64_t row = m0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (row < m_end && col < N) out[row * N + col] = acc[rt][v];
         }
-    if (threadIdx.x == 0) __hip_atomic_store(p.count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sums the split-K partial products in split order: C[i] = sum_s part[s * stride + i],
+// four consecutive elements per thread (slices are 16-byte aligned: stride % 4 == 0); the
+// last total % 4 elements are done by the first threads of workgroup 0.
+__global__ __launch_bounds__(256) void w4a16_split_reduce(const float *__restrict__ part, float *__restrict__ C,
+                                                          int64_t total, int64_t stride, int splits)
+{
+    const int64_t n4 = total / 4;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        f32x4 acc = *(const f32x4 *)(part + 4 * i);
+        for (int s2 = 1; s2 < splits; ++s2) acc += *(const f32x4 *)(part + (int64_t)s2 * stride + 4 * i);
+        *(f32x4 *)(C + 4 * i) = acc;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < total - 4 * n4) {
+        const int64_t e = 4 * n4 + threadIdx.x;
+        float acc = part[e];
+        for (int s2 = 1; s2 < splits; ++s2) acc += part[(int64_t)s2 * stride + e];
+        C[e] = acc;
+    }
 }
 
 __global__ __launch_bounds__(256) void w4_pack_kernel(const uint8_t *__restrict__ q,
@@ -928,14 +904,13 @@ Choice score(const Variant &v, int64_t base, int groups, int splits)
 // or more, smaller row blocks (more tiles for narrow outputs, each weight dequantized once
 // per block), times every K split.  The score is a small cost model in microseconds:
 //   rounds of resident workgroups x groups per split x time per group
-//   + split-K handoff (partial stores, arrival count, the last workgroup reading every
-//     split's partial tile back)
+//   + split-K reduction (a second launch reading every split's partial product)
 // where the time per group is the larger of the matrix-core time and the VALU time
 // (dequantization, rescale and MFMA issue) of one workgroup, at a sustained efficiency.
 constexpr double kLargeClockGHz = 2.4;
-constexpr double kLargeEff = 0.8;          // sustained fraction of the issue-limited rate
-constexpr double kUsLargeHandoff = 2.0;    // partial stores, arrival count
-constexpr double kLargeReadGBs = 150.0;    // one workgroup reading partial tiles back
+constexpr double kLargeEff = 0.44;         // sustained fraction of the issue-limited rate (measured)
+constexpr double kUsLargeReduce = 2.5;     // second launch (split reduction) and its ramp
+constexpr double kLargeReduceGBs = 4000.0; // split reduction: partial reads + C writes
 constexpr int kLargeMinM = 64;
 
 bool large_path(int64_t M, int64_t /*N*/) { return M >= kLargeMinM; }
@@ -953,26 +928,24 @@ void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     const int n_tiles = (int)((N + kLTileN - 1) / kLTileN);
     const int min_blocks = (int)((M + kLMaxRT * 32 - 1) / (kLMaxRT * 32));
     double best_us = 1e30;
-    int best_mb = min_blocks, best_s = 1, best_rows = 0, best_rt = kLMaxRT;
+    int best_mb = min_blocks, best_s = 1, best_rows = 0;
     for (int mbk = min_blocks; mbk <= 2 * min_blocks; ++mbk) {
         const int rows = (int)((M + mbk - 1) / mbk);
         const int rt = (rows + 31) / 32;
         if (rt < 2 || (int64_t)(mbk - 1) * rows >= M) continue;
         const int64_t base = (int64_t)mbk * n_tiles;
         const double tg = large_group_us(rt);
-        const double part_us = (double)rt * 32 * kLTileN * 4 / (kLargeReadGBs * 1e3);
         for (int sp = 1; sp <= groups; ++sp) {
             const int gps = (groups + sp - 1) / sp;
             if ((groups + gps - 1) / gps != sp) continue;
             const int64_t rounds = (base * sp + kCUs - 1) / kCUs;
             double us = (double)rounds * gps * tg;
-            if (sp > 1) us += kUsLargeHandoff + sp * part_us;
+            if (sp > 1) us += kUsLargeReduce + (double)(sp + 1) * M * N * 4 / (kLargeReduceGBs * 1e3);
             if (us < best_us) {
                 best_us = us;
                 best_mb = mbk;
                 best_s = sp;
                 best_rows = rows;
-                best_rt = rt;
             }
         }
     }
@@ -986,7 +959,7 @@ void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->splits = best_s;
     pl->groups_per_split = gps;
     pl->workgroups = base * best_s;
-    pl->workspace_bytes = best_s > 1 ? base * 4 + base * best_s * (int64_t)best_rt * 32 * kLTileN * 4 : 0;
+    pl->workspace_bytes = best_s > 1 ? best_s * ((M * N + 3) / 4 * 4) * 4 : 0;
 }
 
 void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
@@ -1089,8 +1062,9 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
     hipStream_t s = (hipStream_t)stream;
     unsigned *count = nullptr;
     float *part = nullptr;
-    if (pl.splits > 1) {
-        const int64_t tiles = (int64_t)pl.n_tiles * pl.m_blocks;
+    if (pl.workspace_bytes > 0) {
+        // small-M: [tile counters][partial tiles]; large-M: [split slices] only
+        const int64_t tiles = pl.kernel == 3 ? 0 : (int64_t)pl.n_tiles * pl.m_blocks;
         st = get_workspace(dev, s, (size_t)tiles, (size_t)(pl.workspace_bytes - tiles * 4), &count, &part);
         if (st != W4_OK) return st;
     }
@@ -1103,7 +1077,7 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
         q.Z = zeros_u4;
         q.C = C;
         q.part = part;
-        q.count = count;
+        q.stride = (M * N + 3) / 4 * 4;
         q.M = M;
         q.K = K;
         q.N = N;
@@ -1121,6 +1095,15 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
         default: W4_LAUNCH_L(5); break;
         }
 #undef W4_LAUNCH_L
+        if (pl.splits > 1) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail("w4a16_gemm launch", e);
+            const int64_t n4 = M * N / 4;
+            int64_t blocks = (n4 + 255) / 256;
+            blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+            hipLaunchKernelGGL(w4a16_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, C, M * N, q.stride,
+                               pl.splits);
+        }
     } else {
         SmallParams p;
         p.A = (const uint16_t *)A_bf16;
