@@ -664,13 +664,15 @@ void w4a16_mfma_kernel(LargeParams p)
             // writes spread over the group instead of queueing behind its reads at the end
             *(u32x4 *)(lds + (buf ^ 1) * kBuf + alds[rt]) = ar[rt];
         }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[RT - 1][v] = __builtin_fmaf(sc, Q[v], acc[RT - 1][v]);
         scn = scale_of(Wn);
         // ... and keep it from sinking into the next group: the operands are complete here.
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Bn[ks]));
+        // The barrier comes as soon as this wave's LDS traffic for the group is done; the
+        // last row tile's rescale (which waits for its MFMAs) follows it.
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[RT - 1][v] = __builtin_fmaf(sc, Q[v], acc[RT - 1][v]);
         __builtin_amdgcn_sched_barrier(0);
     };
 
