@@ -305,15 +305,15 @@ __device__ __forceinline__ void compute_pipe(const PipeRegs<AV> &r, const char *
     }
     f32x4 P[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) P[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
     for (int st = 0; st < 4; ++st) {
-        f16x8 a_op = __builtin_bit_cast(f16x8, u32x4{0, 0, 0, 0});
-        if (c < mv) a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_wave + c * kARowBytes + (4 * st + kq) * 16));
+        // rows mv..15 of the tile are zero (cleared once, never staged)
+        const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_wave + c * kARowBytes + (4 * st + kq) * 16));
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const f16x8 b_op = unpack8(r.w[st][t], zlo[t], zhi[t], magic);
-            P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, P[t], 0, 0, 0);
+            // the first k-step starts from a literal zero accumulator (no register clearing)
+            const f32x4 c_in = st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[t];
+            P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, c_in, 0, 0, 0);
         }
     }
     const int4 xr = *(const int4 *)(lds_wave + kPipeExpOffset + 16 * kq);
@@ -365,8 +365,11 @@ void w4a16_kernel(SmallParams p)
         row = row < mv ? row : mv - 1;
         aoff[i] = (uint32_t)(((int64_t)(m0 + row) * p.K + (lane & 15) * 8) * 2);
     }
-    // rows 4*AV..15 of this wave's exponent table are never staged: they read as 0
+    // rows 4*AV..15 of this wave's exponent table are never staged: they read as 0; rows
+    // mv..15 of its activation tile are never staged either: they read as 0 in the MFMAs
     if (4 * AV < kTileM && lane >= 4 * AV && lane < kTileM) *(int *)(tile_lds + kPipeExpOffset + 4 * lane) = 0;
+    for (int i = lane; i < (kTileM - mv) * (kARowBytes / 16); i += kWave)
+        *(u32x4 *)(tile_lds + mv * kARowBytes + i * 16) = u32x4{0u, 0u, 0u, 0u};
 
     f32x4 acc[4];
 #pragma unroll
