@@ -868,17 +868,22 @@ w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N)
     return W4_OK;
 }
 
-// Launch plan.  Every workgroup of a launch should be resident at once (a second, partly
-// filled round would double the time); the rest is a small cost model in microseconds:
-//   launch + first-byte latency + max(streaming time, per-wave compute) + split-K handoff
-// where the streaming rate is limited by the bytes the resident waves keep in flight
-// (about one group each, over the loaded HBM latency) and by the achievable HBM rate.
-// Both kernel shapes and every split count are scored; the cheapest wins.
+// Small-M launch plan.  Every workgroup of a launch must be resident at once (a second,
+// partly filled round would double the time).  Each candidate (workgroup shape x split
+// count) is scored with a cost model in microseconds, fitted to measured launches:
+//   launch and first bytes + max(streaming time, per-wave compute) + split-K handoff
+// where the per-wave compute is the groups a wave walks in turn times the time of one group
+// at the CU's wave count, the streaming rate is limited by the bytes the waves keep in
+// flight over the loaded latency (and by the achievable rate), and the handoff grows with
+// the number of partial tiles the last workgroup sums.  At (nearly) equal cost the shape
+// with more waves in flight wins.
 constexpr double kUsLaunch = 3.5;        // dispatch + first bytes from HBM
-constexpr double kUsLatency = 1.6;       // loaded HBM latency seen by one wave
-constexpr double kGBsPeak = 6200.0;      // achievable streaming rate for this access pattern
-constexpr double kUsHandoff = 3.0;       // split-K: partial stores, arrival count, reload
-constexpr double kUsPerGroup = 0.55;     // one wave's compute for one group
+constexpr double kUsLatency = 1.0;       // loaded latency seen by the in-flight bytes
+constexpr double kGBsPeak = 4500.0;      // achievable streaming rate of one launch
+constexpr double kUsHandoff = 1.0;       // split-K: partial stores, arrival count
+constexpr double kUsPerSplit = 0.4;      // ... and reading back one partial tile
+constexpr double kUsPerGroup = 0.5;      // one group per wave, per wave resident on its SIMD
+constexpr double kRowsFactor = 0.3;      // extra group cost per 4 rows beyond the first 4
 constexpr int kGroupBytes = 16 * 4 * kTileN;  // packed weights of one wave-group
 
 struct Choice {
@@ -887,21 +892,24 @@ struct Choice {
     double us;
 };
 
-Choice score(const Variant &v, int64_t base, int groups, int splits)
+Choice score(const Variant &v, int64_t base, int groups, int splits, int av, int64_t K, int64_t N)
 {
     Choice c = {&v, splits, 1e30};
     const int gps = (groups + splits - 1) / splits;
     const int64_t wgs = base * splits;
     if (wgs > (int64_t)v.per_cu * kCUs) return c;
+    const int64_t wg_per_cu = (wgs + kCUs - 1) / kCUs;  // on the busiest CU
+    const double waves_per_simd = (double)v.waves * wg_per_cu / 4;
+    const double t_group = kUsPerGroup * waves_per_simd * (1.0 + kRowsFactor * (av - 1));
     const int per_wave = (gps + v.waves - 1) / v.waves;
+    const double compute = per_wave * t_group;
     const int active_waves_per_wg = gps < v.waves ? gps : v.waves;
-    const double inflight = (double)wgs * active_waves_per_wg * kGroupBytes;
+    const double inflight = (double)wgs * active_waves_per_wg * (per_wave < 2 ? per_wave : 2) * kGroupBytes;
     double rate = inflight / (kUsLatency * 1e-6) / 1e9;  // GB/s
     if (rate > kGBsPeak) rate = kGBsPeak;
-    const double bytes = (double)base * groups * kGroupBytes;
-    const double stream = bytes / (rate * 1e3);  // us
-    const double compute = per_wave * kUsPerGroup;
-    c.us = kUsLaunch + (stream > compute ? stream : compute) + (splits > 1 ? kUsHandoff : 0.0);
+    const double stream = (double)K * N * 0.5234375 / (rate * 1e3);  // us
+    c.us = kUsLaunch + (stream > compute ? stream : compute) +
+           (splits > 1 ? kUsHandoff + kUsPerSplit * splits : 0.0);
     return c;
 }
 
@@ -974,10 +982,13 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     const int m_blocks = (int)((M + kTileM - 1) / kTileM);
     const int64_t base = (int64_t)n_tiles * m_blocks;
     Choice best = {&kWide, 1, 1e30};  // fallback (more tiles than resident slots): wide, no split
-    for (const Variant *v : {&kWide, &kTall}) {
+    const int av = (int)(((M < kTileM ? M : kTileM) + 3) / 4);
+    for (const Variant *v : {&kTall, &kWide}) {  // tall first: it keeps near-ties
         for (int sp = 1; sp <= groups; ++sp) {
-            const Choice c = score(*v, base, groups, sp);
-            if (c.us < best.us) best = c;
+            const int gps = (groups + sp - 1) / sp;
+            if ((groups + gps - 1) / gps != sp) continue;
+            const Choice c = score(*v, base, groups, sp, av, K, N);
+            if (c.us < best.us * 0.98) best = c;
         }
     }
     const int gps = (groups + best.splits - 1) / best.splits;

@@ -398,3 +398,18 @@ def test_large_m_graph_and_reproducible():
         torch.cuda.synchronize()
         for e, o in zip(eager, outs):
             assert torch.equal(e, o), f"replay {rep} differs from eager"
+
+
+@pytest.mark.parametrize("M,K,N", [(65, 8192, 3), (97, 4096, 131), (161, 2048, 2049), (70, 8192, 1)])
+def test_large_m_split_odd_sizes(orc, M, K, N):
+    # split-K plans whose M*N is not a multiple of 4 exercise the reduction's tail path
+    p = w4.plan(M, K, N)
+    assert p["kernel"] == 3 and p["splits"] > 1
+    log(f"large split odd M={M} K={K} N={N} plan={p}")
+    x = synth.generate_custom(M, K, N, seed=30)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    C = run(to_dev(x), out=out).cpu().numpy()
+    assert np.all(np.isfinite(C))
+    cols = np.unique(np.r_[0, N - 1, np.random.default_rng(31).integers(0, N, 24)])
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+    check(C[:, cols], Cr, Cabs, f"large split odd M={M} K={K} N={N}")
