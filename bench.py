@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen2.5-7b-verify-m5")
+    ap.add_argument("--copies", type=int, default=1,
+                    help="repeat the workload's GEMMs this many times with distinct weights in one step "
+                         "(e.g. 512 copies of the single GEMM exceed the on-chip caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--eager-steps", type=int, default=0,
@@ -107,7 +110,7 @@ def main():
         log(f"copy probe: 5 copies of {args.copy_probe_mib} MiB")
         return
 
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.with_copies(synth.WORKLOADS[args.workload], args.copies)
     t0 = time.time()
     gemms = []  # (spec, device tensors, out)
     host_sample = []
@@ -246,6 +249,7 @@ def main():
         "config": {
             "workload": args.workload,
             "gemms_per_step": len(gemms),
+            "copies": args.copies,
             "M": sorted({s.M for s, _ in gemms}),
             "weight_bytes_per_step": wl.weight_bytes,
             "hip_graph": graph is not None,

@@ -147,6 +147,20 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
+def with_copies(wl: Workload, copies: int) -> Workload:
+    """The workload's GEMMs repeated `copies` times back to back, each copy with its own
+    weights and activations (copy 0 is the workload itself).  Used to measure a small
+    workload from HBM rather than from the on-chip caches."""
+    if copies <= 1:
+        return wl
+    gemms = []
+    for c in range(copies):
+        for g in wl.gemms:
+            seed = (g.seed[0], g.seed[1], g.seed[2] + 100000 * c) + tuple(g.seed[3:])
+            gemms.append(dataclasses.replace(g, name=f"{g.name}.copy{c}", seed=seed))
+    return Workload(f"{wl.name}-x{copies}", f"{wl.description}, {copies} distinct copies", tuple(gemms))
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round finite float32 values to bfloat16 (nearest, ties to even); return the u16 bits."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
