@@ -90,8 +90,11 @@ typedef struct w4_plan {
     int m_blocks;           /* row blocks of tile_m                                          */
     int n_tiles;            /* column tiles of tile_n                                        */
     int splits;             /* K splits across workgroups (1 = no workspace)                */
-    int groups_per_split;   /* 128-wide K groups handled by one workgroup                   */
-    int64_t workgroups;     /* grid size                                                     */
+    int groups_per_split;   /* 128-wide K groups handled by one workgroup of a split tile    */
+    int full_tiles;         /* kernel 1: tiles 0..full_tiles-1 (row-block-major order) run
+                               unsplit, one workgroup each, and only the other tiles are
+                               split (a multiple of 256: whole rounds of CUs); 0 otherwise  */
+    int64_t workgroups;     /* grid size: full_tiles + (m_blocks*n_tiles - full_tiles)*splits */
     int64_t workspace_bytes;/* split-K workspace needed (0 when splits == 1)                 */
 } w4_plan;
 

@@ -60,6 +60,7 @@ class Plan(ctypes.Structure):
         ("n_tiles", ctypes.c_int),
         ("splits", ctypes.c_int),
         ("groups_per_split", ctypes.c_int),
+        ("full_tiles", ctypes.c_int),
         ("workgroups", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
     ]

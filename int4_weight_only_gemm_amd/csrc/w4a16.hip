@@ -77,10 +77,11 @@ struct SmallParams {
     const uint16_t *S;
     const uint8_t *Z;
     float *C;
-    float *part;        // [m_blocks * n_tiles][splits][16][64] float32 partials
-    unsigned *count;    // [m_blocks * n_tiles] arrival counters, zero between calls
+    float *part;        // [split tiles][splits][16][64] float32 partials
+    unsigned *count;    // [split tiles] arrival counters, zero between calls
     int64_t M, K, N;
     int groups, splits, gps, n_tiles, m_blocks;
+    int full_tiles;     // tiles [0, full_tiles) are not split (a multiple of 8)
 };
 
 // ------------------------------------------------------------------------------------
@@ -334,9 +335,23 @@ void w4a16_kernel(SmallParams p)
     extern __shared__ __attribute__((aligned(16))) char lds[];  // per-wave tiles, then reduction
     __shared__ int s_last;
 
-    const uint32_t logical = xcd_local_id(blockIdx.x, gridDim.x);
-    const int sp = (int)(logical % (uint32_t)p.splits);
-    const uint32_t tile = logical / (uint32_t)p.splits;
+    // Tiles [0, full_tiles) run unsplit, one workgroup each, and are dispatched first; the
+    // other tiles are split `splits` ways.  full_tiles is a multiple of 8, so both ranges
+    // start on XCD 0 and each spreads evenly over the XCDs (and over the CUs of an XCD).
+    const uint32_t nfull = (uint32_t)p.full_tiles;
+    uint32_t tile;
+    int sp, gps;
+    if (blockIdx.x < nfull) {
+        tile = xcd_local_id(blockIdx.x, nfull);
+        sp = 0;
+        gps = p.groups;
+    } else {
+        const uint32_t logical = xcd_local_id(blockIdx.x - nfull, gridDim.x - nfull);
+        tile = nfull + logical / (uint32_t)p.splits;
+        sp = (int)(logical % (uint32_t)p.splits);
+        gps = p.gps;
+    }
+    const bool split = tile >= nfull && p.splits > 1;
     const int nt = (int)(tile % (uint32_t)p.n_tiles);
     const int mb = (int)(tile / (uint32_t)p.n_tiles);
     const int n0 = nt * kTileN, m0 = mb * kTileM;
@@ -345,8 +360,8 @@ void w4a16_kernel(SmallParams p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
     const int c = lane & 15, kq = lane >> 4;
 
-    const int g_begin = sp * p.gps;
-    const int g_end = min(p.groups, g_begin + p.gps);
+    const int g_begin = sp * gps;
+    const int g_end = min(p.groups, g_begin + gps);
     const int g0 = g_begin + wave;
     const int n_my = g0 < g_end ? (g_end - g0 + WAVES - 1) / WAVES : 0;
     char *tile_lds = lds + wave * kPipeWaveBytes;
@@ -432,11 +447,12 @@ void w4a16_kernel(SmallParams p)
                 if (col + t < p.N) dst[t] = v[t];
         }
     };
-    if (p.splits == 1) {
+    if (!split) {
         if (valid) store_c(sum);
         return;
     }
-    float *tile_part = p.part + (int64_t)tile * p.splits * (kTileM * kTileN);
+    const uint32_t stile = tile - nfull;  // index among the split tiles
+    float *tile_part = p.part + (int64_t)stile * p.splits * (kTileM * kTileN);
     if (valid) {
         float *dst = tile_part + (int64_t)sp * (kTileM * kTileN) + row * kTileN + 4 * quad;
 #pragma unroll
@@ -445,7 +461,7 @@ void w4a16_kernel(SmallParams p)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(p.count + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned prev = __hip_atomic_fetch_add(p.count + stile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (unsigned)(p.splits - 1));
     }
     __syncthreads();
@@ -460,7 +476,7 @@ void w4a16_kernel(SmallParams p)
         }
         store_c(tot);
     }
-    if (threadIdx.x == 0) __hip_atomic_store(p.count + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(p.count + stile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------------------------
@@ -885,6 +901,7 @@ constexpr double kUsPerSplit = 0.4;      // ... and reading back one partial til
 constexpr double kUsPerGroup = 0.5;      // one group per wave, per wave resident on its SIMD
 constexpr double kRowsFactor = 0.3;      // extra group cost per 4 rows beyond the first 4
 constexpr int kGroupBytes = 16 * 4 * kTileN;  // packed weights of one wave-group
+constexpr int kMinPartGroups = 4;        // balanced wide plan: groups per split part, at least
 
 struct Choice {
     const Variant *v;
@@ -971,6 +988,7 @@ void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->n_tiles = n_tiles;
     pl->splits = best_s;
     pl->groups_per_split = gps;
+    pl->full_tiles = 0;
     pl->workgroups = base * best_s;
     pl->workspace_bytes = best_s > 1 ? best_s * ((M * N + 3) / 4 * 4) * 4 : 0;
 }
@@ -991,8 +1009,28 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
             if (c.us < best.us * 0.98) best = c;
         }
     }
+    // Balanced wide plan.  When the plain wide plan wins and its tiles fill r whole rounds of
+    // CUs (r workgroups on every CU) plus a remainder, the busiest CUs hold r + 1 whole
+    // tiles.  Instead, r*256 tiles run unsplit (dispatched first, r per CU) and the remaining
+    // tiles are split over the slots still free, so that a CU holds r whole tiles and at
+    // most one split part.  The parts finish early, keeping their handoff off the critical
+    // path; each keeps at least kMinPartGroups groups, below which the handoff and the
+    // extra launch width cost more than the balance gains (measured).
+    int64_t full = 0;
+    const int r = (int)(base / kCUs);
+    if (best.v == &kWide && best.splits == 1 && r >= 1 && r < kWide.per_cu && base % kCUs != 0) {
+        const int64_t rem = base - (int64_t)r * kCUs;
+        int64_t sp = (int64_t)kCUs * (kWide.per_cu - r) / rem;
+        sp = sp < groups / kMinPartGroups ? sp : groups / kMinPartGroups;
+        if (sp >= 2) {
+            const int g = (int)((groups + sp - 1) / sp);
+            best.splits = (groups + g - 1) / g;
+            full = (int64_t)r * kCUs;
+        }
+    }
     const int gps = (groups + best.splits - 1) / best.splits;
     const int splits = (groups + gps - 1) / gps;
+    const int64_t split_tiles = splits > 1 ? base - full : 0;
     pl->kernel = best.v == &kTall ? 2 : 1;
     pl->tile_m = kTileM;
     pl->tile_n = kTileN;
@@ -1000,8 +1038,9 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->n_tiles = n_tiles;
     pl->splits = splits;
     pl->groups_per_split = gps;
-    pl->workgroups = base * splits;
-    pl->workspace_bytes = splits > 1 ? base * 4 + base * splits * kTileM * kTileN * 4 : 0;
+    pl->full_tiles = (int)full;
+    pl->workgroups = full + (base - full) * splits;
+    pl->workspace_bytes = split_tiles * 4 + split_tiles * splits * kTileM * kTileN * 4;
 }
 
 // M >= 64 with N even runs on the bf16 matrix-core kernel; everything else on the
@@ -1080,7 +1119,7 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
     float *part = nullptr;
     if (pl.workspace_bytes > 0) {
         // small-M: [tile counters][partial tiles]; large-M: [split slices] only
-        const int64_t tiles = pl.kernel == 3 ? 0 : (int64_t)pl.n_tiles * pl.m_blocks;
+        const int64_t tiles = pl.kernel == 3 ? 0 : (int64_t)pl.n_tiles * pl.m_blocks - pl.full_tiles;
         st = get_workspace(dev, s, (size_t)tiles, (size_t)(pl.workspace_bytes - tiles * 4), &count, &part);
         if (st != W4_OK) return st;
     }
@@ -1137,6 +1176,7 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
         p.gps = pl.groups_per_split;
         p.n_tiles = pl.n_tiles;
         p.m_blocks = pl.m_blocks;
+        p.full_tiles = pl.full_tiles;
         const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros_u4, 4);
         const size_t lds = plan_lds_bytes(M, pl);
         const int rows = M < kTileM ? (int)M : kTileM;

@@ -65,7 +65,8 @@ def test_pack_validation():
 
 
 def test_plan_covers_shapes():
-    # every shape of the synthetic workloads has a valid plan that tiles N and K exactly
+    # every shape of the synthetic workloads has a valid plan that tiles N and K exactly;
+    # a balanced wide plan runs whole rounds of 256 tiles unsplit and splits the rest
     import synth
     seen = set()
     for wl in synth.WORKLOADS.values():
@@ -85,8 +86,14 @@ def test_plan_covers_shapes():
             assert p["m_blocks"] * p["tile_m"] >= g.M > (p["m_blocks"] - 1) * p["tile_m"]
             assert p["splits"] * p["groups_per_split"] >= groups
             assert (p["splits"] - 1) * p["groups_per_split"] < groups
-            assert p["workgroups"] == p["n_tiles"] * p["m_blocks"] * p["splits"]
+            tiles = p["n_tiles"] * p["m_blocks"]
+            full = p["full_tiles"]
+            assert full % 256 == 0 and 0 <= full < tiles
+            assert full == 0 or (p["kernel"] == 1 and p["splits"] > 1)
+            assert p["workgroups"] == full + (tiles - full) * p["splits"]
             assert (p["workspace_bytes"] > 0) == (p["splits"] > 1)
+            if p["kernel"] in (1, 2):  # every workgroup resident at once
+                assert p["workgroups"] <= 256 * (3 if p["kernel"] == 1 else 1) or p["splits"] == 1
     with pytest.raises(w4.W4Error):
         w4.plan(5, 100, 64)
 

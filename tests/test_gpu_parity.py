@@ -65,6 +65,31 @@ def test_split_k_shapes(orc, M, K, N):
     check(C[:, cols], Cr, Cabs, f"split M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N", [(5, 1024, 19200), (20, 1024, 9600), (3, 2048, 19198), (1, 3584, 37888)])
+def test_balanced_wide_plan(orc, M, K, N):
+    # whole rounds of unsplit tiles plus split remainder tiles: both kinds of workgroup, the
+    # split tiles' counters and partials, row blocks crossing the boundary, ragged N
+    p = w4.plan(M, K, N)
+    log(f"balanced M={M} K={K} N={N} plan={p}")
+    assert p["kernel"] == 1 and p["full_tiles"] > 0 and p["splits"] > 1
+    x = synth.generate_custom(M, K, N, seed=21)
+    dev = to_dev(x)
+    C1 = run(dev)
+    C2 = run(dev)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2), "balanced plan not reproducible"
+    C = C1.cpu().numpy()
+    if M * K * N <= 400_000_000:
+        cols = None
+        Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
+    else:  # full-size shape: both column ranges, every split boundary's neighbourhood
+        cols = np.unique(np.r_[0, 64 * p["full_tiles"] - 1, 64 * p["full_tiles"], N - 1,
+                               np.random.default_rng(22).integers(0, N, 96)])
+        Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+        C = C[:, cols]
+    check(C, Cr, Cabs, f"balanced M={M} K={K} N={N}")
+
+
 # ----------------------------------------------------------------- exact special cases
 @pytest.mark.parametrize("M,K,N", [(5, 384, 72), (16, 1152, 64), (1, 4096, 33)])
 def test_one_hot_bitwise(orc, M, K, N):
