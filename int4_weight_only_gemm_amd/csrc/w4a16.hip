@@ -57,6 +57,8 @@ constexpr int kGroup = 128;                // quantization group along K
 constexpr int kChunksPerRow = kGroup / 8;  // 16-byte activation chunks per group row
 constexpr int kARowBytes = (kChunksPerRow + 1) * 16;  // +16 bytes of padding: conflict-free reads
 constexpr int kCacheStream = 2;            // buffer-load cache policy: non-temporal (streamed once)
+constexpr int kCacheCoherent = 16;         // buffer-op cache policy: device-coherent (sc1), as for
+                                           // agent-scope atomics on this target
 constexpr int kCUs = 256;
 
 // Two shapes of the same kernel.  "Wide": 4 waves per workgroup, 3 workgroups resident per
@@ -451,13 +453,17 @@ void w4a16_kernel(SmallParams p)
         if (valid) store_c(sum);
         return;
     }
+    // Partials travel as 16-byte device-coherent stores and loads (the cache policy of
+    // agent-scope atomics), one per lane and split.
     const uint32_t stile = tile - nfull;  // index among the split tiles
-    float *tile_part = p.part + (int64_t)stile * p.splits * (kTileM * kTileN);
-    if (valid) {
-        float *dst = tile_part + (int64_t)sp * (kTileM * kTileN) + row * kTileN + 4 * quad;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) __hip_atomic_store(dst + t, sum[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const int64_t split_tiles = (int64_t)p.m_blocks * p.n_tiles - nfull;
+    const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)p.part, (short)0, (int)(split_tiles * p.splits * (kTileM * kTileN * 4)), kRsrcWord3);
+    constexpr uint32_t kPartBytes = kTileM * kTileN * 4;  // one split's partial tile
+    const uint32_t lane_part = (uint32_t)stile * (uint32_t)p.splits * kPartBytes + (uint32_t)(row * kTileN + 4 * quad) * 4;
+    if (valid)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sum), prs, lane_part + (uint32_t)sp * kPartBytes,
+                                               0, kCacheCoherent);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -468,11 +474,19 @@ void w4a16_kernel(SmallParams p)
     if (!s_last) return;
     asm volatile("" ::: "memory");
     if (valid) {
+        // up to kBatch splits' partials in flight at once, summed in split order
+        constexpr int kBatch = 8;
         f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-        for (int sp2 = 0; sp2 < p.splits; ++sp2) {
-            const float *src = tile_part + (int64_t)sp2 * (kTileM * kTileN) + row * kTileN + 4 * quad;
+        for (int b = 0; b < p.splits; b += kBatch) {
+            u32x4 v[kBatch];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) tot[t] += __hip_atomic_load(src + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < kBatch; ++i) {
+                const int s2 = b + i < p.splits ? b + i : p.splits - 1;  // clamped: no branch around loads
+                v[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, lane_part + (uint32_t)s2 * kPartBytes, 0, kCacheCoherent);
+            }
+#pragma unroll
+            for (int i = 0; i < kBatch; ++i)
+                if (b + i < p.splits) tot += __builtin_bit_cast(f32x4, v[i]);
         }
         store_c(tot);
     }
