@@ -259,15 +259,17 @@ template <bool VEC, int AV>
 __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources &rs, const LaneOffsets<VEC> &o,
                                           const uint32_t (&aoff)[AV], int g, PipeRegs<AV> &r)
 {
+    // activations first: their conversion needs only them, and can run while the
+    // weights are still in flight (loads complete in issue order)
+#pragma unroll
+    for (int i = 0; i < AV; ++i)
+        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[i], (uint32_t)g * (kGroup * 2), 0);
     GroupRegs w;
     load_group<VEC>(p, rs, o, g, w);
 #pragma unroll
     for (int st = 0; st < 4; ++st) r.w[st] = w.w[st];
     r.s = w.s;
     r.z = w.z;
-#pragma unroll
-    for (int i = 0; i < AV; ++i)
-        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[i], (uint32_t)g * (kGroup * 2), 0);
 }
 
 // Convert this wave's group of activations into its LDS tile: row r scaled by 2^x[r],
