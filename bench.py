@@ -10,10 +10,11 @@ synchronization, timed with HIP events on the launch stream.
 Printed (one JSON line): effective weight GB/s (weight bytes = 4-bit codes + fp16 scales
 + u8 zeros per 128, i.e. 0.5234375 B per weight, divided by the step time), the fraction
 of the 8 TB/s HBM peak, the dominant kernel's roofline figures (its average launch duration
-over the timed region, HBM traffic per launch from counters when a matching summary exists)
-and the oracle timed on the host cores on a bounded sample.
+over the timed region, HBM traffic per launch from counters when a matching summary exists),
+the oracle timed on the host cores on a bounded sample, and the achievable read ceiling: the
+library's streaming-read probe over the same byte counts, one launch per GEMM, in a graph.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-ceiling]
 """
 from __future__ import annotations
 
@@ -38,6 +39,7 @@ KERNEL_NAME_LARGE = "w4a16_mfma_kernel"  # M >= 64: bf16 matrix cores
 # "key: value" lines); used only while the kernel source hash and workload still match.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_w4a16_kernel_qwen2.5-7b-verify-m5.md")
 CPU_SAMPLE_SECONDS = 10.0
+PROBE_BLOCKS = 768  # streaming-read probe: three workgroups of 256 lanes per CU
 
 
 def log(msg):
@@ -77,6 +79,7 @@ def parse():
                     help="repeat the workload's GEMMs this many times with distinct weights in one step "
                          "(e.g. 512 copies of the single GEMM exceed the on-chip caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--eager-steps", type=int, default=0,
                     help="only run this many eager steps (for a profiler) and print nothing else")
@@ -209,6 +212,49 @@ def main():
 
     traffic = read_traffic(args.workload)
 
+    ceiling = None
+    if not args.no_ceiling:
+        # Achievable HBM read rate for this step's byte counts: the streaming-read probe reads
+        # one buffer per GEMM holding exactly that GEMM's weight bytes (codes, scales, zeros),
+        # one launch per GEMM, captured and replayed like the step.
+        sizes = [(spec.weight_bytes + 15) // 16 * 16 for spec, _ in gemms]
+        region = torch.empty(sum(sizes) // 4, dtype=torch.int32, device=dev)
+        sink = torch.empty((PROBE_BLOCKS, 4), dtype=torch.int32, device=dev)
+        base, offs = region.data_ptr(), []
+        for n in sizes:
+            offs.append(base)
+            base += n
+
+        def probe_step():
+            for ptr, n in zip(offs, sizes):
+                w4.read_probe_raw(ptr, n, sink.data_ptr(), PROBE_BLOCKS, handle)
+
+        with torch.cuda.stream(stream):
+            probe_step()
+        torch.cuda.synchronize()
+        pgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pgraph, stream=stream):
+            probe_step()
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                pgraph.replay()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for _ in range(args.steps):
+                pgraph.replay()
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        probe_ms = ev0.elapsed_time(ev1) / args.steps
+        cgbs = sum(sizes) / (probe_ms * 1e-3) / 1e9
+        ceiling = {"kind": "streaming-read probe", "value": round(cgbs, 2), "unit": "GB/s",
+                   "frac_of_peak": round(cgbs / HBM_PEAK_GBS, 4),
+                   "gemm_over_ceiling": round(gbs / cgbs, 4),
+                   "ms_per_step": round(probe_ms, 5), "launches_per_step": len(sizes), "blocks": PROBE_BLOCKS}
+        log(f"streaming-read ceiling: {cgbs:.1f} GB/s ({probe_ms:.4f} ms per step); GEMM step at "
+            f"{100 * gbs / cgbs:.1f}% of it")
+        del pgraph, region
+
     cpu = None
     if not args.no_cpu_baseline:
         # The oracle as it stands, on the host cores, over whole GEMMs of this workload taken
@@ -266,6 +312,7 @@ def main():
             "launches_timed": launches,
         },
         "cpu_baseline": cpu,
+        "ceiling": ceiling,
     }
     print(json.dumps(out), flush=True)
 

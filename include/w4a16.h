@@ -79,6 +79,21 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
  */
 w4_status w4_pack(const uint8_t *q_u4, uint32_t *Wq, int64_t K, int64_t N, void *stream);
 
+/*
+ * Streaming-read probe (a measurement aid, not part of the GEMM): reads `bytes` bytes at
+ * `src` once, with the weight stream's load policy (16-byte non-temporal loads, several in
+ * flight per lane), so that its rate is the achievable HBM read ceiling for a buffer of that
+ * size.
+ *   src: device, 16-byte aligned, 16 <= bytes < 2^31 and bytes % 16 == 0 (not modified).
+ *   xor_out: device [blocks][4] uint32, 4-byte aligned, overwritten: entry [b][w] is the
+ *     XOR of the 32-bit words read by wave w of block b (each 16-byte chunk is read by
+ *     exactly one wave), so the XOR over all entries equals the XOR of every word of the
+ *     buffer.
+ *   blocks: workgroups of 256 lanes, 1..65535 (768 fills three per CU).
+ * Asynchronous on `stream`; validation errors as for w4a16_gemm.
+ */
+w4_status w4_read_probe(const void *src, int64_t bytes, uint32_t *xor_out, int64_t blocks, void *stream);
+
 /* How w4a16_gemm would run a shape (host only, no HIP call). */
 typedef struct w4_plan {
     int kernel;             /* 1 = small-M wide (4 waves per workgroup, fp16 MFMA),

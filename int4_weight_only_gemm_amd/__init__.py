@@ -75,6 +75,8 @@ _lib.w4a16_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.w4a16_gemm.restype = ctypes.c_int
 _lib.w4_pack.argtypes = [_vp, _vp, _i64, _i64, _vp]
 _lib.w4_pack.restype = ctypes.c_int
+_lib.w4_read_probe.argtypes = [_vp, _i64, _vp, _i64, _vp]
+_lib.w4_read_probe.restype = ctypes.c_int
 _lib.w4a16_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(Plan)]
 _lib.w4a16_plan.restype = ctypes.c_int
 _lib.w4_status_string.argtypes = [ctypes.c_int]
@@ -178,3 +180,32 @@ def pack(q, out=None, stream=None):
     if rc:
         raise W4Error(rc, "w4_pack")
     return out
+
+
+def read_probe(buf, blocks: int = 768, out=None, stream=None):
+    """Streaming-read probe over a contiguous device tensor (size a multiple of 16 bytes).
+
+    Returns the int32 [blocks, 4] per-wave XORs of the 32-bit words read (4 waves per
+    block); XOR-reducing all of them gives the XOR of every word of the buffer.
+    """
+    import torch
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty((blocks, 4), dtype=torch.int32, device=buf.device)
+    else:
+        _check(out, "out", torch.int32, 2)
+        if tuple(out.shape) != (blocks, 4):
+            raise ValueError("out must be int32 [blocks, 4]")
+    rc = _lib.w4_read_probe(buf.data_ptr(), nbytes, out.data_ptr(), blocks, _stream_handle(stream))
+    if rc:
+        raise W4Error(rc, "w4_read_probe")
+    return out
+
+
+def read_probe_raw(src_ptr: int, nbytes: int, out_ptr: int, blocks: int, stream_handle: int = 0) -> None:
+    """Direct C-ABI call of the streaming-read probe on raw device pointers."""
+    rc = _lib.w4_read_probe(src_ptr, nbytes, out_ptr, blocks, stream_handle)
+    if rc:
+        raise W4Error(rc, "w4_read_probe")

@@ -777,6 +777,37 @@ __global__ __launch_bounds__(256) void w4_pack_kernel(const uint8_t *__restrict_
     }
 }
 
+// Streaming-read probe: the achievable HBM read rate for a buffer of a given size, as a
+// ceiling for the weight stream.  Each lane keeps four 16-byte non-temporal buffer loads in
+// flight (the weight stream's load policy) over a grid-stride loop and XORs what it reads;
+// each wave writes the XOR of the 32-bit words it read, so a caller can check that every
+// chunk was read once.  Loads past the end read the last chunk again (no branch around a load) and are
+// dropped from the XOR.
+__global__ __launch_bounds__(256) void w4_read_probe_kernel(const void *src, uint32_t n16, uint32_t *__restrict__ out)
+{
+    constexpr int kUnroll = 4;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, (int)(n16 * 16), kRsrcWord3);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    const uint32_t stride = gridDim.x * 256 * kUnroll;
+    for (uint32_t base = blockIdx.x * 256 * kUnroll + threadIdx.x; base < n16; base += stride) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t i = base + u * 256;
+            v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (i < n16 ? i : n16 - 1) * 16, 0, kCacheStream);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (base + u * 256 < n16) acc ^= v[u];
+    }
+    // XOR of the lane's words, then across the wave (cross-lane shuffles, no barrier); lane 0
+    // writes the wave's value
+    uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off, 64);
+    if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)] = x;
+}
+
 // ------------------------------------------------------------------------------------
 // Host side
 
@@ -1211,6 +1242,31 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("w4a16_gemm launch", e);
+    return W4_OK;
+}
+
+w4_status w4_read_probe(const void *src, int64_t bytes, uint32_t *xor_out, int64_t blocks, void *stream)
+{
+    if (!src || !xor_out) {
+        set_error("w4_read_probe: a required pointer is NULL");
+        return W4_ERR_NULL;
+    }
+    if (bytes < 16 || bytes % 16 != 0 || bytes >= ((int64_t)1 << 31) || blocks < 1 || blocks > 65535) {
+        set_error("w4_read_probe: bytes=%lld blocks=%lld: need 16<=bytes<2^31, bytes%%16==0, 1<=blocks<=65535",
+                  (long long)bytes, (long long)blocks);
+        return W4_ERR_SHAPE;
+    }
+    if (!aligned(src, 16) || !aligned(xor_out, 4)) {
+        set_error("w4_read_probe: src must be 16-byte aligned and xor_out 4-byte aligned");
+        return W4_ERR_ALIGN;
+    }
+    int dev = -1;
+    w4_status st = check_device(&dev);
+    if (st != W4_OK) return st;
+    hipLaunchKernelGGL(w4_read_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       src, (uint32_t)(bytes / 16), xor_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("w4_read_probe launch", e);
     return W4_OK;
 }
 

@@ -64,6 +64,21 @@ def test_pack_validation():
     assert lib.w4_pack(A16, W16 + 2, 8, 4, None) == 3
 
 
+def test_read_probe_validation():
+    lib = w4.lib()
+    probe = lib.w4_read_probe
+    probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert probe(None, 64, W16, 4, None) == 1
+    assert probe(A16, 64, None, 4, None) == 1
+    assert probe(A16, 40, W16, 4, None) == 2   # not a multiple of 16
+    assert probe(A16, 0, W16, 4, None) == 2
+    assert probe(A16, 64, W16, 0, None) == 2
+    assert probe(A16, 1 << 31, W16, 4, None) == 2
+    assert probe(A16, 64, W16, 65536, None) == 2
+    assert probe(A16 + 8, 64, W16, 4, None) == 3
+    assert probe(A16, 64, W16 + 2, 4, None) == 3
+
+
 def test_plan_covers_shapes():
     # every shape of the synthetic workloads has a valid plan that tiles N and K exactly;
     # a balanced wide plan runs whole rounds of 256 tiles unsplit and splits the rest

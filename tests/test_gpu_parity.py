@@ -33,6 +33,21 @@ def test_pack_bit_exact(orc, K, N):
     assert np.array_equal(Wq.cpu().numpy().view(np.uint32), orc.pack(q))
 
 
+@pytest.mark.parametrize("nbytes,blocks", [(32, 768), (48, 1), ((1 << 20) + 48, 7), ((1 << 24) + 4096, 768)])
+def test_read_probe_reads_every_chunk(nbytes, blocks):
+    # the streaming-read probe's per-wave XORs combine to the XOR of every word of the buffer
+    log(f"read probe bytes={nbytes} blocks={blocks}")
+    host = np.random.default_rng(nbytes).integers(0, 1 << 32, nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    out = w4.read_probe(buf, blocks=blocks)
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32).ravel())
+    assert got == np.bitwise_xor.reduce(host)
+    # a probe over all but the last chunk misses exactly that chunk's words
+    out = w4.read_probe(buf[: nbytes // 4 - 4], blocks=blocks)
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32).ravel())
+    assert got == np.bitwise_xor.reduce(host[:-4])
+
+
 # ------------------------------------------------------------------- tiny-shape grid
 GRID_M = [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 17, 63, 64, 65, 160]
 GRID_K = [128, 256, 384, 1152]
