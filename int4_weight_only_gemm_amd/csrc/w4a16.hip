@@ -124,6 +124,17 @@ __device__ __forceinline__ int chunk_max_exp(u32x4 v)
     return (int)(max(c.x, c.y) >> 7);
 }
 
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in every lane: rotations
+// by 8, 4, 2 and 1 within the row, without LDS traffic.
+__device__ __forceinline__ int row16_max(int e)
+{
+    e = max(e, __builtin_amdgcn_update_dpp(0, e, 0x128, 0xF, 0xF, false));  // row_ror:8
+    e = max(e, __builtin_amdgcn_update_dpp(0, e, 0x124, 0xF, 0xF, false));  // row_ror:4
+    e = max(e, __builtin_amdgcn_update_dpp(0, e, 0x122, 0xF, 0xF, false));  // row_ror:2
+    e = max(e, __builtin_amdgcn_update_dpp(0, e, 0x121, 0xF, 0xF, false));  // row_ror:1
+    return e;
+}
+
 __device__ __forceinline__ uint32_t pack_h2(float a, float b)
 {
     f16x2 h = {(_Float16)a, (_Float16)b};
@@ -283,9 +294,7 @@ __device__ __forceinline__ void stage_pipe(const PipeRegs<AV> &r, char *lds_wave
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
         const int row = 4 * i + (lane >> 4);
-        int e = chunk_max_exp(r.a[i]);
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) e = max(e, __shfl_xor(e, off, 16));
+        const int e = row16_max(chunk_max_exp(r.a[i]));
         const int x = 142 - max(e, 1);
         if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = convert_chunk(r.a[i], x);
         if (kc == 0) *(int *)(lds_wave + kPipeExpOffset + 4 * row) = row < mv ? x : 0;
