@@ -105,6 +105,27 @@ def test_balanced_wide_plan(orc, M, K, N):
     check(C, Cr, Cabs, f"balanced M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N", [(5, 65536, 65528), (64, 65536, 65528), (63, 1 << 24, 1), (8191, 131072, 8)])
+def test_maximum_sizes(orc, M, K, N):
+    # the largest arrays the kernels' 32-bit byte offsets address: packed weights
+    # (K/8*N*4) or activations (M*K*2) just under 2 GiB, on both kernels; sampled rows and
+    # columns (edges, row-block and tile boundaries) against the oracle
+    assert K // 8 * N * 4 < 1 << 31 and M * K * 2 < 1 << 31
+    p = w4.plan(M, K, N)
+    log(f"maximum size M={M} K={K} N={N} plan={p}")
+    x = synth.generate_custom(M, K, N, seed=31)
+    dev = to_dev(x)
+    C = run(dev).cpu().numpy()
+    del dev
+    rng = np.random.default_rng(32)
+    rows = np.unique(np.r_[0, M - 1, [r for r in (15, 16, 159, 160, 4095) if r < M],
+                           rng.integers(0, M, 4)]).astype(np.int64)
+    cols = np.unique(np.r_[0, N - 1, [c for c in (63, 64, 255, 256) if c < N],
+                           rng.integers(0, N, 24)]).astype(np.int64)
+    Cr, Cabs = orc.gemm(x.A[rows], x.Wq, x.S, x.Z, cols=cols)
+    check(C[np.ix_(rows, cols)], Cr, Cabs, f"max size M={M} K={K} N={N}")
+
+
 # ----------------------------------------------------------------- exact special cases
 @pytest.mark.parametrize("M,K,N", [(5, 384, 72), (16, 1152, 64), (1, 4096, 33)])
 def test_one_hot_bitwise(orc, M, K, N):
