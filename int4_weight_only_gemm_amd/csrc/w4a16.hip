@@ -9,7 +9,8 @@
 // which is how the kernels below evaluate it: the inner sums use exact (q - z) factors
 // and float32 accumulation, the outer sum applies each group's scale once per output.
 //
-// Hardware mapping (MI355X, CDNA4):
+// Hardware mapping (MI355X, CDNA4), small M (M < 64; M >= 64, and large GEMMs from M = 33,
+// run the bf16 matrix-core kernel further down):
 //  * Weights are streamed once from HBM with 16-byte non-temporal loads; a lane's load
 //    holds four adjacent columns of one packed row (8 codes each).
 //  * (q - z) is built in registers as exact binary16 pairs: a code is OR-ed into the
@@ -25,7 +26,8 @@
 //  * Split-K across workgroups writes float32 partials to a workspace with device-coherent
 //    stores; a per-tile arrival counter elects the last workgroup, which sums the partials
 //    in split order, writes C and resets the counter.  One launch per GEMM, no memset, no
-//    cache flush, bitwise reproducible.
+//    cache flush, bitwise reproducible.  A plan may run whole rounds of tiles unsplit and
+//    split only the remaining tiles, to balance the CUs.
 
 #include <hip/hip_runtime.h>
 
@@ -505,11 +507,11 @@ void w4a16_kernel(SmallParams p)
 }
 
 // ------------------------------------------------------------------------------------
-// Large-M kernel (batched verify, M >= 64): a dense contraction on the bfloat16 matrix
-// cores (v_mfma_f32_32x32x16_bf16).  A workgroup owns a row block of up to RT*32 rows and
-// 256 columns; each of its 8 waves owns 32 columns, one per lane pair (lane l holds column
-// l % 32 and k-half l / 32 of every B operand), so every weight is loaded and dequantized
-// once per workgroup and reused by all RT row tiles.
+// Large-M kernel (batched verify: M >= 64, and large GEMMs from M = 33): a dense
+// contraction on the bfloat16 matrix cores (v_mfma_f32_32x32x16_bf16).  A workgroup owns
+// a row block of up to RT*32 rows and 256 columns; each of its 8 waves owns 32 columns,
+// one per lane pair (lane l holds column l % 32 and k-half l / 32 of every B operand), so
+// every weight is loaded and dequantized once per workgroup and reused by all RT row tiles.
 //
 // (q - z) is formed exactly in bfloat16: the codes of a word are biased into bytes
 // (0x80 | q) so that subtracting z cannot borrow across bytes, the bias is removed with
@@ -997,9 +999,21 @@ constexpr double kLargeClockGHz = 2.4;
 constexpr double kLargeEff = 0.44;         // sustained fraction of the issue-limited rate (measured)
 constexpr double kUsLargeReduce = 2.5;     // second launch (split reduction) and its ramp
 constexpr double kLargeReduceGBs = 4000.0; // split reduction: partial reads + C writes
+// Which kernel: from M = 64 on, every shape runs on the bf16 kernel (the small-M kernel
+// would dequantize each weight once per 16-row block).  From M = 33 (two 32-row tiles
+// hold the rows) the bf16 kernel also wins on large GEMMs, where its one dequantization per
+// weight outweighs the padded rows; on narrow outputs it needs deep K splits and their
+// reduction, and the small-M kernel stays faster (measured at M = 40..63 on the 7B layer
+// shapes: K*N of 68M and 136M favour the bf16 kernel by 10-40%, K*N of 13M and 17M favour
+// the small-M kernel by 30-35%).
 constexpr int kLargeMinM = 64;
+constexpr int kLargeMidM = 33;
+constexpr int64_t kLargeMidWeights = (int64_t)1 << 25;  // K*N at which 33 <= M < 64 goes large
 
-bool large_path(int64_t M, int64_t /*N*/) { return M >= kLargeMinM; }
+bool large_path(int64_t M, int64_t K, int64_t N)
+{
+    return M >= kLargeMinM || (M >= kLargeMidM && K * N >= kLargeMidWeights);
+}
 
 double large_group_us(int rt)
 {
@@ -1099,11 +1113,11 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->workspace_bytes = split_tiles * 4 + split_tiles * splits * kTileM * kTileN * 4;
 }
 
-// M >= 64 with N even runs on the bf16 matrix-core kernel; everything else on the
+// Shapes chosen by large_path run on the bf16 matrix-core kernel; everything else on the
 // small-M kernel (row blocks of 16).
 void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 {
-    if (large_path(M, N))
+    if (large_path(M, K, N))
         make_large_plan(M, K, N, pl);
     else
         make_small_plan(M, K, N, pl);

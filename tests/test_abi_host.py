@@ -79,6 +79,18 @@ def test_read_probe_validation():
     assert probe(A16, 64, W16 + 2, 4, None) == 3
 
 
+def test_kernel_choice_by_shape():
+    # bf16 kernel from M = 64; from M = 33 only for large GEMMs (K*N >= 2^25)
+    assert w4.plan(63, 128, 64)["kernel"] in (1, 2)
+    assert w4.plan(64, 128, 64)["kernel"] == 3
+    assert w4.plan(32, 4096, 8192)["kernel"] in (1, 2)
+    assert w4.plan(33, 4096, 8192)["kernel"] == 3
+    assert w4.plan(40, 4096, 8191)["kernel"] in (1, 2)
+    assert w4.plan(40, 3584, 4608)["kernel"] in (1, 2)
+    assert w4.plan(40, 3584, 37888)["kernel"] == 3
+    assert w4.plan(63, 18944, 3584)["kernel"] == 3
+
+
 def test_plan_covers_shapes():
     # every shape of the synthetic workloads has a valid plan that tiles N and K exactly;
     # a balanced wide plan runs whole rounds of 256 tiles unsplit and splits the rest
@@ -92,7 +104,7 @@ def test_plan_covers_shapes():
             seen.add(key)
             p = w4.plan(*key)
             groups = g.K // 128
-            assert (p["kernel"] == 3) == (g.M >= 64)
+            assert (p["kernel"] == 3) == (g.M >= 64 or (g.M >= 33 and g.K * g.N >= 1 << 25))
             if p["kernel"] == 3:
                 assert p["tile_n"] == 256 and p["tile_m"] <= 160
             else:

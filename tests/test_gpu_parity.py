@@ -105,6 +105,22 @@ def test_balanced_wide_plan(orc, M, K, N):
     check(C, Cr, Cabs, f"balanced M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N", [(33, 4096, 8192), (37, 4096, 8193), (40, 4096, 8200), (63, 18944, 3584),
+                                   (48, 3584, 37888)])
+def test_mid_m_bf16_path(orc, M, K, N):
+    # 33 <= M < 64 on large GEMMs runs the bf16 kernel: a row block of M rows in two 32-row
+    # tiles (rows past M masked), ragged and odd N, deep K splits
+    p = w4.plan(M, K, N)
+    log(f"mid-M bf16 path M={M} K={K} N={N} plan={p}")
+    assert p["kernel"] == 3
+    x = synth.generate_custom(M, K, N, seed=41)
+    C = run(to_dev(x)).cpu().numpy()
+    cols = np.unique(np.r_[0, 255, 256, N - 257, N - 256, N - 1,
+                           np.random.default_rng(42).integers(0, N, 96)]).astype(np.int64)
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+    check(C[:, cols], Cr, Cabs, f"mid-M M={M} K={K} N={N}")
+
+
 @pytest.mark.parametrize("M,K,N", [(5, 65536, 65528), (64, 65536, 65528), (63, 1 << 24, 1), (8191, 131072, 8)])
 def test_maximum_sizes(orc, M, K, N):
     # the largest arrays the kernels' 32-bit byte offsets address: packed weights
