@@ -34,7 +34,7 @@ METRIC = "W4A16 verify-GEMM effective weight GB/s and % of HBM roofline at M=gam
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(ROOT, "int4_weight_only_gemm_amd", "csrc", "w4a16.hip")
 KERNEL_NAME = "w4a16_kernel"           # small M: fp16 matrix cores, exact (q - z) operands
-KERNEL_NAME_LARGE = "w4a16_mfma_kernel"  # M >= 64 (and large GEMMs from M = 33): bf16 matrix cores
+KERNEL_NAME_LARGE = "w4a16_mfma_kernel"  # M >= 64 (and large GEMMs from M = 17): bf16 matrix cores
 # HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE passes (a text summary with
 # "key: value" lines); used only while the kernel source hash and workload still match.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_w4a16_kernel_qwen2.5-7b-verify-m5.md")

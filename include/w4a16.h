@@ -22,7 +22,7 @@
  * Accuracy contract: every element satisfies
  *     |C - C_exact| <= 1e-4 * sum_k |A[m,k] * W[k,n]| + 1e-6.
  * The (q - z) factors and their products with A are exact; partial sums are float32.
- * M >= 64, and 33 <= M < 64 with K*N >= 2^25, run on the bfloat16 matrix cores with A
+ * M >= 64, and 17 <= M < 64 with K*N >= 2^25, run on the bfloat16 matrix cores with A
  * used as given.  Other shapes run on the
  * binary16 matrix cores with A rescaled by a power of two per (row, 128-wide group), so
  * that the group's largest |A| lands in [2^15, 2^16); elements more than 2^33 below that
@@ -99,10 +99,10 @@ w4_status w4_read_probe(const void *src, int64_t bytes, uint32_t *xor_out, int64
 typedef struct w4_plan {
     int kernel;             /* 1 = small-M wide (4 waves per workgroup, fp16 MFMA),
                                2 = small-M tall (12 waves, fp16 MFMA),
-                               3 = large-M (M >= 64, or M >= 33 with K*N >= 2^25:
+                               3 = large-M (M >= 64, or M >= 17 with K*N >= 2^25:
                                    8 waves, bf16 MFMA)                                       */
-    int tile_m;             /* output rows per row block (16 for kernels 1, 2; at most 160
-                               for kernel 3, computed in row tiles of 32)                    */
+    int tile_m;             /* output rows per row block (16 for kernels 1, 2; 1 to 160 for
+                               kernel 3, computed in row tiles of 32)                        */
     int tile_n;             /* output columns per workgroup tile (64, or 256 for kernel 3)   */
     int m_blocks;           /* row blocks of tile_m                                          */
     int n_tiles;            /* column tiles of tile_n                                        */

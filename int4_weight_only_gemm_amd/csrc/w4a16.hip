@@ -9,7 +9,7 @@
 // which is how the kernels below evaluate it: the inner sums use exact (q - z) factors
 // and float32 accumulation, the outer sum applies each group's scale once per output.
 //
-// Hardware mapping (MI355X, CDNA4), small M (M < 64; M >= 64, and large GEMMs from M = 33,
+// Hardware mapping (MI355X, CDNA4), small M (M < 64; M >= 64, and large GEMMs from M = 17,
 // run the bf16 matrix-core kernel further down):
 //  * Weights are streamed once from HBM with 16-byte non-temporal loads; a lane's load
 //    holds four adjacent columns of one packed row (8 codes each).
@@ -507,7 +507,7 @@ void w4a16_kernel(SmallParams p)
 }
 
 // ------------------------------------------------------------------------------------
-// Large-M kernel (batched verify: M >= 64, and large GEMMs from M = 33): a dense
+// Large-M kernel (batched verify: M >= 64, and large GEMMs from M = 17): a dense
 // contraction on the bfloat16 matrix cores (v_mfma_f32_32x32x16_bf16).  A workgroup owns
 // a row block of up to RT*32 rows and 256 columns; each of its 8 waves owns 32 columns,
 // one per lane pair (lane l holds column l % 32 and k-half l / 32 of every B operand), so
@@ -531,7 +531,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kLWaves = 8;
 constexpr int kLTileN = kLWaves * 32;  // 256 columns per workgroup
-constexpr int kLMaxRT = 5;             // up to 160 rows per workgroup (row tiles of 32)
+constexpr int kLMaxRT = 5;             // 32 to 160 rows per workgroup (row tiles of 32)
 constexpr int kLThreads = kLWaves * kWave;
 
 struct LargeParams {
@@ -1000,15 +1000,15 @@ constexpr double kLargeEff = 0.44;         // sustained fraction of the issue-li
 constexpr double kUsLargeReduce = 2.5;     // second launch (split reduction) and its ramp
 constexpr double kLargeReduceGBs = 4000.0; // split reduction: partial reads + C writes
 // Which kernel: from M = 64 on, every shape runs on the bf16 kernel (the small-M kernel
-// would dequantize each weight once per 16-row block).  From M = 33 (two 32-row tiles
-// hold the rows) the bf16 kernel also wins on large GEMMs, where its one dequantization per
-// weight outweighs the padded rows; on narrow outputs it needs deep K splits and their
-// reduction, and the small-M kernel stays faster (measured at M = 40..63 on the 7B layer
-// shapes: K*N of 68M and 136M favour the bf16 kernel by 10-40%, K*N of 13M and 17M favour
-// the small-M kernel by 30-35%).
+// would dequantize each weight once per 16-row block).  From M = 17 (more than one 16-row
+// block) the bf16 kernel also wins on large GEMMs, where its one dequantization per weight
+// outweighs the padded rows; on narrow outputs it needs deep K splits and their reduction,
+// and the small-M kernel stays faster (measured at M = 17..63 on the 7B layer shapes: K*N
+// of 68M and 136M favour the bf16 kernel by up to 40% or tie, K*N of 13M and 17M favour
+// the small-M kernel by 20-35%).
 constexpr int kLargeMinM = 64;
-constexpr int kLargeMidM = 33;
-constexpr int64_t kLargeMidWeights = (int64_t)1 << 25;  // K*N at which 33 <= M < 64 goes large
+constexpr int kLargeMidM = 17;
+constexpr int64_t kLargeMidWeights = (int64_t)1 << 25;  // K*N at which 17 <= M < 64 goes large
 
 bool large_path(int64_t M, int64_t K, int64_t N)
 {
@@ -1032,7 +1032,8 @@ void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     for (int mbk = min_blocks; mbk <= 2 * min_blocks; ++mbk) {
         const int rows = (int)((M + mbk - 1) / mbk);
         const int rt = (rows + 31) / 32;
-        if (rt < 2 || (int64_t)(mbk - 1) * rows >= M) continue;
+        // one-tile blocks only where all rows fit one tile (17 <= M <= 32)
+        if ((rt < 2 && M > 32) || (int64_t)(mbk - 1) * rows >= M) continue;
         const int64_t base = (int64_t)mbk * n_tiles;
         const double tg = large_group_us(rt);
         for (int sp = 1; sp <= groups; ++sp) {
@@ -1214,6 +1215,7 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
         q.block_rows = pl.tile_m;
 #define W4_LAUNCH_L(RTV) hipLaunchKernelGGL((w4a16_mfma_kernel<RTV>), grid, dim3(kLThreads), 0, s, q)
         switch ((pl.tile_m + 31) / 32) {
+        case 1: W4_LAUNCH_L(1); break;
         case 2: W4_LAUNCH_L(2); break;
         case 3: W4_LAUNCH_L(3); break;
         case 4: W4_LAUNCH_L(4); break;

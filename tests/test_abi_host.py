@@ -80,10 +80,12 @@ def test_read_probe_validation():
 
 
 def test_kernel_choice_by_shape():
-    # bf16 kernel from M = 64; from M = 33 only for large GEMMs (K*N >= 2^25)
+    # bf16 kernel from M = 64; from M = 17 only for large GEMMs (K*N >= 2^25)
     assert w4.plan(63, 128, 64)["kernel"] in (1, 2)
     assert w4.plan(64, 128, 64)["kernel"] == 3
-    assert w4.plan(32, 4096, 8192)["kernel"] in (1, 2)
+    assert w4.plan(16, 4096, 8192)["kernel"] in (1, 2)
+    assert w4.plan(17, 4096, 8192)["kernel"] == 3
+    assert w4.plan(32, 4096, 8192)["kernel"] == 3
     assert w4.plan(33, 4096, 8192)["kernel"] == 3
     assert w4.plan(40, 4096, 8191)["kernel"] in (1, 2)
     assert w4.plan(40, 3584, 4608)["kernel"] in (1, 2)
@@ -104,7 +106,7 @@ def test_plan_covers_shapes():
             seen.add(key)
             p = w4.plan(*key)
             groups = g.K // 128
-            assert (p["kernel"] == 3) == (g.M >= 64 or (g.M >= 33 and g.K * g.N >= 1 << 25))
+            assert (p["kernel"] == 3) == (g.M >= 64 or (g.M >= 17 and g.K * g.N >= 1 << 25))
             if p["kernel"] == 3:
                 assert p["tile_n"] == 256 and p["tile_m"] <= 160
             else:

@@ -105,11 +105,11 @@ def test_balanced_wide_plan(orc, M, K, N):
     check(C, Cr, Cabs, f"balanced M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("M,K,N", [(33, 4096, 8192), (37, 4096, 8193), (40, 4096, 8200), (63, 18944, 3584),
-                                   (48, 3584, 37888)])
+@pytest.mark.parametrize("M,K,N", [(17, 4096, 8192), (24, 18944, 3584), (32, 4096, 8193), (33, 4096, 8192),
+                                   (37, 4096, 8193), (40, 4096, 8200), (63, 18944, 3584), (48, 3584, 37888)])
 def test_mid_m_bf16_path(orc, M, K, N):
-    # 33 <= M < 64 on large GEMMs runs the bf16 kernel: a row block of M rows in two 32-row
-    # tiles (rows past M masked), ragged and odd N, deep K splits
+    # 17 <= M < 64 on large GEMMs runs the bf16 kernel: a row block of M rows in one or two
+    # 32-row tiles (rows past M masked), ragged and odd N, deep K splits
     p = w4.plan(M, K, N)
     log(f"mid-M bf16 path M={M} K={K} N={N} plan={p}")
     assert p["kernel"] == 3
