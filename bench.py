@@ -195,15 +195,20 @@ def main():
     tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, {gbs:.1f} GB/s, {tflops:.2f} TFLOP/s")
 
-    # Roofline figures of the dominant kernel: every launch of a step is w4a16_gemm's kernel,
-    # so its average launch duration is the timed region (HIP events on the launch stream)
-    # divided by the launches it holds, and the algorithmic bytes (or flops) per launch are
-    # the step's totals divided by the same count.
+    # Roofline figures of the dominant kernel.  The bound follows the step's arithmetic
+    # intensity against the ridge of the two peaks (2*M flops per 0.5234375 weight bytes:
+    # matrix-core-bound from M ~ 82 on); the named kernel is the one streaming most of the
+    # step's weight bytes.  Its average launch duration is the timed region (HIP events on
+    # the launch stream) divided by the launches it holds, and the algorithmic bytes (or
+    # flops) per launch are the step's totals divided by the same count.
     launches = args.steps * len(calls)
     avg_dur_s = elapsed_ms * 1e-3 / launches
-    # the step's dominant kernel: the bf16 matrix-core kernel if any GEMM of the step runs on it
-    mfma_bound = any(w4.plan(spec.M, spec.K, spec.N)["kernel"] == 3 for spec, _ in gemms)
-    if mfma_bound:  # batched verify: a dense contraction, priced against the bf16 MFMA peak
+    kinds = [w4.plan(spec.M, spec.K, spec.N)["kernel"] for spec, _ in gemms]
+    large_bytes = sum(spec.weight_bytes for (spec, _), k in zip(gemms, kinds) if k == 3)
+    kernel = KERNEL_NAME_LARGE if 2 * large_bytes > wl.weight_bytes else KERNEL_NAME
+    dtype = "bf16" if all(k == 3 for k in kinds) else ("f16" if all(k != 3 for k in kinds) else "f16+bf16")
+    mfma_bound = wl.flops / wl.weight_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:  # a dense contraction, priced against the bf16 MFMA peak
         achieved = wl.flops / len(calls) / avg_dur_s / 1e12
         peak, unit, bound = MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     else:
@@ -289,7 +294,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if mfma_bound else "f16",
+        "dtype": dtype,
         "data": "synthetic",
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "tflops": round(tflops, 3),
@@ -303,7 +308,7 @@ def main():
         },
         "roofline": {
             "bound": bound,
-            "kernel": KERNEL_NAME_LARGE if mfma_bound else KERNEL_NAME,
+            "kernel": kernel,
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": unit,

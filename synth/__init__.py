@@ -9,7 +9,8 @@ Workload shapes come from the models the pages measure:
   * "When Do Quantized Drafts Help Speculative Decoding?", section "Current pilot setup":
     a Qwen2.5-7B-Instruct target verifying a Qwen2.5-1.5B-Instruct draft at gamma=4, batch 1;
     the interpretation item (c) sweeps gamma over 2..6.
-  * the same page, section "What is open": Llama2-7B at batch 32, the batched regime.
+  * the same page, section "What is open": Llama2-7B at batch 32, the batched regime, and
+    whether the ceiling holds at batch 8 and 16 (the Qwen2.5-7B verify at 40 and 80 rows).
   * "The Free Half of Speculative Decoding", third paragraph: the target is quantized to
     INT4 with AWQ (weight-only), the draft may be quantized as well.
 The per-layer (K, N) sizes are the public architectures of those models (hidden size,
@@ -137,6 +138,18 @@ WORKLOADS: Dict[str, Workload] = {
             "qwen2.5-7b-gamma-sweep",
             "Qwen2.5-7B down (18944x3584) and gate_up (3584x37888), 28 copies each, M in 3..7",
             _gamma_sweep(4),
+        ),
+        Workload(
+            "qwen2.5-7b-batched-verify-m40",
+            "batched verify of a Qwen2.5-7B-shaped target, batch 8 x (gamma+1) = 40 rows, "
+            "28 layers x {qkv,o,gate_up,down}",
+            _model_pass(6, "qwen2.5-7b", 40, 28),
+        ),
+        Workload(
+            "qwen2.5-7b-batched-verify-m80",
+            "batched verify of a Qwen2.5-7B-shaped target, batch 16 x (gamma+1) = 80 rows, "
+            "28 layers x {qkv,o,gate_up,down}",
+            _model_pass(7, "qwen2.5-7b", 80, 28),
         ),
         Workload(
             "llama2-7b-batched-verify-m160",

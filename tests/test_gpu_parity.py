@@ -343,7 +343,8 @@ def test_workload_single_m5_full(orc):
     check(C, Cr, Cabs, "single-m5")
 
 
-@pytest.mark.parametrize("name", ["qwen2.5-1.5b-draft-m1", "qwen2.5-7b-verify-m5", "llama2-7b-batched-verify-m160"])
+@pytest.mark.parametrize("name", ["qwen2.5-1.5b-draft-m1", "qwen2.5-7b-verify-m5", "qwen2.5-7b-batched-verify-m40",
+                                  "qwen2.5-7b-batched-verify-m80", "llama2-7b-batched-verify-m160"])
 def test_workload_layer_sampled(orc, name):
     wl = synth.WORKLOADS[name]
     for spec in wl.gemms[:4]:  # one layer: every projection shape of the model
