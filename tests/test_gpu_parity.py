@@ -261,7 +261,8 @@ def test_back_to_back_shapes_reproducible(orc):
 
 
 def test_graph_replay_matches_eager():
-    shapes = [(5, 3584, 4608), (5, 18944, 3584), (1, 1536, 17920)]
+    # tall split plans, and balanced wide plans (unsplit tiles plus split tiles)
+    shapes = [(5, 3584, 4608), (5, 18944, 3584), (1, 1536, 17920), (5, 3584, 37888)]
     xs = [to_dev(synth.generate_custom(M, K, N, seed=13)) for (M, K, N) in shapes]
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
