@@ -1,4 +1,6 @@
-"""The oracle: a plain fp64 CPU reference for the W4A16 GEMM and its packing rule.
+"""The oracle: a plain fp64 CPU reference for the W4A16 GEMM, its packing rule, and the
+round-to-nearest quantizer that produces the format (binary32, as the pages' format is
+produced; see the C source).
 
 TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check in __graft_entry__ and the
 bench's CPU-baseline leg may import this package. It shares no code with the HIP
@@ -63,6 +65,10 @@ class Oracle:
         lib.oracle_bf16_to_f64.restype = ctypes.c_double
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_w4_quantize.argtypes = [vp, vp, vp, vp, i64, i64]
+        lib.oracle_w4_quantize.restype = ctypes.c_int
         self._lib = lib
 
     # -- decoders -----------------------------------------------------------------
@@ -77,6 +83,27 @@ class Oracle:
         out = np.empty(b.shape, dtype=np.float64)
         self._lib.oracle_decode_f16_array(_ptr(b), _ptr(out), b.size)
         return out
+
+    def f32_to_f16(self, x: float) -> int:
+        """binary16 bits of a binary32 value, ties to even."""
+        return int(self._lib.oracle_f32_to_f16(ctypes.c_float(x)))
+
+    # -- quantizer ----------------------------------------------------------------
+    def quantize(self, W_f16: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+        """Round-to-nearest min/max quantizer (groups of 128 along K), see the C source.
+
+        W_f16: uint16 binary16 bits [K, N].  Returns (Wq uint32 [K/8, N], S uint16 binary16
+        bits [K/128, N], Z uint8 [K/128, N]).
+        """
+        W = np.ascontiguousarray(W_f16, dtype=np.uint16)
+        K, N = W.shape
+        Wq = np.empty((K // 8, N), dtype=np.uint32)
+        S = np.empty((K // 128, N), dtype=np.uint16)
+        Z = np.empty((K // 128, N), dtype=np.uint8)
+        rc = self._lib.oracle_w4_quantize(_ptr(W), _ptr(Wq), _ptr(S), _ptr(Z), K, N)
+        if rc:
+            raise ValueError(f"oracle quantize rejected shape {W.shape}")
+        return Wq, S, Z
 
     # -- packing ------------------------------------------------------------------
     def pack(self, q: np.ndarray) -> np.ndarray:

@@ -179,3 +179,83 @@ int oracle_w4_unpack(const uint32_t *Wq, uint8_t *q, int64_t K, int64_t N)
         for (int64_t n = 0; n < N; ++n) q[k * N + n] = (uint8_t)oracle_code(Wq, N, k, n);
     return 0;
 }
+
+/*
+ * IEEE binary16 encoding of a binary32 value, rounding to nearest with ties to even (the
+ * default rounding of IEEE 754), gradual underflow to subnormals, overflow to infinity.
+ * Written from the format's definition: the value is scaled by a power of two (exact in
+ * binary64) so that the 11 (or fewer, for subnormals) significant bits become an integer,
+ * which rint() rounds in the default ties-to-even mode.
+ */
+uint16_t oracle_f32_to_f16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs((double)x);
+    if (isnan(x)) return (uint16_t)(sign | 0x7E00);
+    if (isinf(x)) return (uint16_t)(sign | 0x7C00);
+    if (a == 0.0) return sign;
+    int e2;
+    frexp(a, &e2);          /* a = f * 2^e2 with f in [0.5, 1): exponent e = e2 - 1 */
+    int e = e2 - 1;
+    if (e < -14) {          /* subnormal range: multiples of 2^-24 */
+        double m = rint(ldexp(a, 24));
+        return (uint16_t)(sign | (uint16_t)m);  /* m = 1024 is the smallest normal */
+    }
+    double m = rint(ldexp(a, 10 - e));  /* in [1024, 2048] */
+    if (m == 2048.0) {
+        m = 1024.0;
+        e += 1;
+    }
+    if (e > 15) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)(m - 1024.0));
+}
+
+/*
+ * The producer side of the storage format: a round-to-nearest min/max quantizer, one
+ * (scale, zero) pair per group of 128 along K and per column, in the GPTQ style the pages
+ * name for their INT4 drafts ("When Do Quantized Drafts Help Speculative Decoding?",
+ * "Current pilot setup" and "What is open": GPTQ/AWQ INT4 weights).  The pages do not
+ * print the rule; this is the plainest asymmetric reading, every step in binary32:
+ *
+ *   lo = min(0, min_k W),  hi = max(0, max_k W)          (the range holds 0, so z fits 0..15)
+ *   s  = binary16((hi - lo) / 15)                         (ties to even)
+ *   if s == 0 (all-zero group, or a range below binary16's resolution): s = binary16(2/15), z = 8
+ *   else z = clamp(rint(-lo / s), 0, 15)
+ *   q  = clamp(rint(W / s) + z, 0, 15)                    (s as stored, rint ties to even)
+ *
+ * W is binary16 [K, N] row-major; outputs are the storage format's Wq [K/8, N] (packed as
+ * oracle_w4_pack), scales [K/128, N] binary16 bits and zeros [K/128, N] (0..15).
+ * Non-finite inputs give unspecified codes (every operation stays defined).
+ */
+int oracle_w4_quantize(const uint16_t *W, uint32_t *Wq, uint16_t *S, uint8_t *Z, int64_t K, int64_t N)
+{
+    if (K < ORACLE_GROUP || K % ORACLE_GROUP != 0 || N < 1) return -1;
+    memset(Wq, 0, (size_t)(K / 8) * (size_t)N * sizeof(uint32_t));
+    for (int64_t g = 0; g < K / ORACLE_GROUP; ++g)
+        for (int64_t n = 0; n < N; ++n) {
+            float lo = 0.0f, hi = 0.0f;
+            for (int64_t k = g * ORACLE_GROUP; k < (g + 1) * ORACLE_GROUP; ++k) {
+                const float w = (float)oracle_f16_to_f64(W[k * N + n]);
+                lo = fminf(lo, w);
+                hi = fmaxf(hi, w);
+            }
+            uint16_t sb = oracle_f32_to_f16((hi - lo) / 15.0f);
+            float s = (float)oracle_f16_to_f64(sb);
+            int z;
+            if (s == 0.0f) {
+                sb = oracle_f32_to_f16(2.0f / 15.0f);
+                s = (float)oracle_f16_to_f64(sb);
+                z = 8;
+            } else {
+                z = (int)fminf(fmaxf(rintf(-lo / s), 0.0f), 15.0f);
+            }
+            S[g * N + n] = sb;
+            Z[g * N + n] = (uint8_t)z;
+            for (int64_t k = g * ORACLE_GROUP; k < (g + 1) * ORACLE_GROUP; ++k) {
+                const float w = (float)oracle_f16_to_f64(W[k * N + n]);
+                const int q = (int)fminf(fmaxf(rintf(w / s) + (float)z, 0.0f), 15.0f);
+                Wq[(k / 8) * N + n] |= (uint32_t)q << (4 * (k % 8));
+            }
+        }
+    return 0;
+}

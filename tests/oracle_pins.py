@@ -16,7 +16,12 @@ What pins what:
     codes), one-hot A (row extraction), q=z and s=0 (exact zeros), exact rational brute
     force with Python fractions on tiny shapes, a BLAS float64 matmul of an explicitly
     dequantized W at a mid size, power-of-two scaling, column sampling and thread-count
-    invariance.
+    invariance;
+  * the binary16 encoder: numpy's IEEE binary32 -> binary16 conversion on every binary16
+    value, every midpoint and random values;
+  * the quantizer: values on the grid (exact scales, zeros and codes), ties at grid
+    midpoints (to even), all-zero and one-signed groups, the half-step error bound and the
+    scale's agreement with the range, power-of-two scaling, column and group permutations.
 """
 from __future__ import annotations
 
@@ -315,7 +320,152 @@ def pin_column_sampling_and_threads(o):
     assert np.array_equal(Cs, C[:, cols]) and np.array_equal(Cabss, Cabs[:, cols])
 
 
+# ---------------------------------------------------------------------------------------
+# The binary16 encoder and the quantizer (the producer side of the format)
+def pin_f16_encoder_against_numpy(o):
+    """binary32 -> binary16 must match numpy's IEEE conversion (ties to even): every
+    binary16 value, every midpoint between neighbours, the overflow and underflow edges
+    and random binary32 values."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    fin = h[np.isfinite(h)].astype(np.float64)
+    vals = np.unique(fin)
+    mids = (vals[:-1] + vals[1:]) / 2  # exact in binary64; representable in binary32
+    rng = np.random.default_rng(5)
+    rnd = np.r_[rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+                65504.0, 65519.99, 65520.0, 1e6, 2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -26, 2.0 ** -14,
+                2.0 ** -14 - 2.0 ** -25, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11]
+    x32 = np.r_[vals, mids, -mids, rnd].astype(np.float32)
+    with np.errstate(over="ignore"):
+        want = x32.astype(np.float16).view(np.uint16)
+    got = np.array([o.f32_to_f16(float(v)) for v in x32], dtype=np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} encodings differ, first {x32[bad[0]]!r}: {got[bad[0]]:#06x} vs {want[bad[0]]:#06x}"
+
+
+def _grid_group(s, z, reps=8):
+    """128 values on the quantization grid (j - z) * s, j = 0..15, each repeated."""
+    return np.repeat((np.arange(16) - z) * s, reps)
+
+
+GRID_CASES = [(0.5, 6), (0.125, 0), (2.0 ** -10, 15), (3 * 2.0 ** -6, 8), (1.25, 3), (1024.0, 9)]
+
+
+def pin_quantize_grid_exact(o):
+    """Values on the grid (j - z)*s with the grid's ends present: the scale, zero and every
+    code come back exactly (s, 15s and (j-z)s are exact in binary16 here)."""
+    cols = [np.r_[_grid_group(s, z), _grid_group(s, z)[::-1]] for s, z in GRID_CASES]
+    W = np.stack(cols, axis=1)  # K = 256: two groups, the second in reverse order
+    Wq, S, Z = o.quantize(f16_bits(W))
+    q = np.stack([np.r_[np.repeat(np.arange(16), 8), np.repeat(np.arange(16), 8)[::-1]] for _ in GRID_CASES], 1)
+    assert np.array_equal(np_unpack(Wq), q), "codes differ on the grid"
+    assert np.array_equal(S, np.tile(f16_bits([s for s, _ in GRID_CASES]), (2, 1))), "scales differ"
+    assert np.array_equal(Z, np.tile(np.array([z for _, z in GRID_CASES], np.uint8), (2, 1))), "zeros differ"
+
+
+def pin_quantize_ties_to_even(o):
+    """Values halfway between grid points round to the even code offset (ties to even),
+    with the grid's ends present so that s and z are those of the grid."""
+    cols, want = [], []
+    for s, z in GRID_CASES:
+        mid = (np.arange(15) - z + 0.5) * s
+        g = np.r_[-z * s, (15 - z) * s, np.resize(mid, 126)]
+        cols.append(g)
+        r = np.array([round(v) for v in np.resize(np.arange(15) - z + 0.5, 126)])  # Python round: ties to even
+        want.append(np.r_[0, 15, r + z])
+    Wq, S, Z = o.quantize(f16_bits(np.stack(cols, 1)))
+    assert np.array_equal(np_unpack(Wq), np.stack(want, 1).astype(np.uint8)), "ties do not round to even"
+
+
+def pin_quantize_all_zero(o):
+    """An all-zero group (either sign of zero) takes s = binary16(2/15) and z = 8, so every
+    code is 8 and dequantizes to 0 exactly."""
+    W = np.zeros((256, 3), np.float64)
+    bits = f16_bits(W)
+    bits[128:, 1] = 0x8000  # -0.0
+    Wq, S, Z = o.quantize(bits)
+    s215 = np.array([np.float32(2) / np.float32(15)], np.float32).astype(np.float16).view(np.uint16)[0]
+    assert np.all(S == s215) and np.all(Z == 8), "degenerate group parameters"
+    assert np.all(np_unpack(Wq) == 8), "degenerate group codes"
+
+
+def pin_quantize_one_signed_groups(o):
+    """The range always holds 0: an all-positive group gets z = 0 and its largest value code
+    15; an all-negative group with an exact scale gets z = 15 and its smallest value code 0."""
+    rng = np.random.default_rng(6)
+    pos = np.r_[2.0, rng.uniform(1.0, 2.0, 127)].astype(np.float16).astype(np.float64)
+    neg = np.r_[-1.875, -0.5, rng.uniform(-1.875, -0.5, 126)].astype(np.float16).astype(np.float64)
+    Wq, S, Z = o.quantize(f16_bits(np.stack([pos, neg], 1)))
+    q = np_unpack(Wq)
+    assert Z[0, 0] == 0 and q[0, 0] == 15, "all-positive group"
+    assert np_f16_to_f64(S[0, 1]) == 0.125 and Z[0, 1] == 15 and q[0, 1] == 0, "all-negative group"
+    assert q[:, 0].min() >= 7 and q[:, 1].max() <= 11, "codes outside the values' range"
+
+
+def _dequant_error(W, Wq, S, Z):
+    q = np_unpack(Wq).astype(np.float64)
+    K, N = q.shape
+    s = np.repeat(np_f16_to_f64(S), 128, axis=0)
+    z = np.repeat(Z.astype(np.float64), 128, axis=0)
+    return np.abs(W - (q - z) * s), s
+
+
+def pin_quantize_error_bound(o):
+    """Every element dequantizes to within about half a step of its value: the codes are the
+    nearest grid points, and the grid spans the group's range (up to the scale's binary16
+    rounding).  Scales track (max - min)/15 within binary16 rounding; zeros lie in 0..15."""
+    rng = np.random.default_rng(7)
+    K, N = 512, 67
+    mag = 10.0 ** rng.integers(-4, 4, N)
+    W = (rng.standard_normal((K, N)) * mag).astype(np.float16).astype(np.float64)
+    W[:, 5] = np.abs(W[:, 5])
+    W[:, 6] = -np.abs(W[:, 6])
+    Wq, S, Z = o.quantize(f16_bits(W))
+    err, s = _dequant_error(W, Wq, S, Z)
+    assert np.all(err <= 0.51 * s), f"dequantization error {np.max(err / s):.3f} steps"
+    Wg = W.reshape(K // 128, 128, N)
+    rng_ = np.maximum(Wg.max(1), 0) - np.minimum(Wg.min(1), 0)
+    half_ulp = np.maximum(2.0 ** -11 * rng_ / 15, 2.0 ** -25)  # relative, or absolute for subnormals
+    assert np.all(np.abs(np_f16_to_f64(S) - rng_ / 15) <= half_ulp * 1.01), "scale off its range"
+    assert Z.max() <= 15
+
+
+def pin_quantize_power_of_two(o):
+    """Scaling the weights by 2^3 or 2^-3 (exact in binary16 here) leaves codes and zeros
+    unchanged and scales the scales by the same power of two."""
+    rng = np.random.default_rng(8)
+    W = rng.standard_normal((256, 33)).astype(np.float16).astype(np.float64)
+    W[np.abs(W) < 2.0 ** -10] = 0.0  # stay clear of binary16 subnormals when scaled down
+    base = o.quantize(f16_bits(W))
+    for e in (3, -3):
+        Wq, S, Z = o.quantize(f16_bits(W * 2.0 ** e))
+        assert np.array_equal(Wq, base[0]) and np.array_equal(Z, base[2]), f"codes change under 2^{e}"
+        assert np.array_equal(np_f16_to_f64(S), np_f16_to_f64(base[1]) * 2.0 ** e), f"scales under 2^{e}"
+
+
+def pin_quantize_layout(o):
+    """Columns and groups are independent: permuting columns, or swapping two groups of
+    rows, permutes the outputs the same way."""
+    rng = np.random.default_rng(9)
+    W = rng.standard_normal((384, 19)).astype(np.float16).astype(np.float64)
+    Wq, S, Z = o.quantize(f16_bits(W))
+    perm = rng.permutation(19)
+    Wq2, S2, Z2 = o.quantize(f16_bits(W[:, perm]))
+    assert np.array_equal(Wq2, Wq[:, perm]) and np.array_equal(S2, S[:, perm]) and np.array_equal(Z2, Z[:, perm])
+    Wsw = np.r_[W[256:], W[128:256], W[:128]]
+    Wq3, S3, Z3 = o.quantize(f16_bits(Wsw))
+    assert np.array_equal(Wq3, np.r_[Wq[32:], Wq[16:32], Wq[:16]]), "group order"
+    assert np.array_equal(S3, S[::-1]) and np.array_equal(Z3, Z[::-1]), "group order of scales/zeros"
+
+
 ALL_PINS = [
+    pin_f16_encoder_against_numpy,
+    pin_quantize_grid_exact,
+    pin_quantize_ties_to_even,
+    pin_quantize_all_zero,
+    pin_quantize_one_signed_groups,
+    pin_quantize_error_bound,
+    pin_quantize_power_of_two,
+    pin_quantize_layout,
     pin_f16_decoder_exhaustive,
     pin_bf16_decoder_exhaustive,
     pin_pack_golden,

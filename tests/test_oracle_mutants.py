@@ -34,6 +34,21 @@ MUTANTS = {
     "pack_mask_dropped": ("(uint32_t)(q[(8 * kb + j) * N + n] & 0xF)", "(uint32_t)(q[(8 * kb + j) * N + n])"),
     "abs_sum_signed": ("abs_acc[m] += fabs(t);", "abs_acc[m] += t;"),
     "accumulate_in_float": ("acc[m] += t;", "acc[m] = (float)(acc[m] + t);"),
+    # binary16 encoder
+    "f16_enc_truncates": ("double m = rint(ldexp(a, 10 - e));", "double m = floor(ldexp(a, 10 - e));"),
+    "f16_enc_ties_away": ("double m = rint(ldexp(a, 10 - e));", "double m = floor(ldexp(a, 10 - e) + 0.5);"),
+    "f16_enc_exponent_bias": ("(uint16_t)((e + 15) << 10)", "(uint16_t)((e + 16) << 10)"),
+    "f16_enc_no_subnormals": ("double m = rint(ldexp(a, 24));", "double m = 0.0 * rint(ldexp(a, 24));"),
+    # quantizer
+    "quant_codes_ties_away": ("rintf(w / s) + (float)z", "roundf(w / s) + (float)z"),
+    "quant_codes_floor": ("rintf(w / s) + (float)z", "floorf(w / s) + (float)z"),
+    "quant_range_without_zero": ("float lo = 0.0f, hi = 0.0f;", "float lo = INFINITY, hi = -INFINITY;"),
+    "quant_sixteen_steps": ("oracle_f32_to_f16((hi - lo) / 15.0f)", "oracle_f32_to_f16((hi - lo) / 16.0f)"),
+    "quant_zero_sign": ("rintf(-lo / s)", "rintf(lo / s)"),
+    "quant_zero_truncated": ("rintf(-lo / s)", "truncf(-lo / s)"),
+    "quant_degenerate_zero": ("                z = 8;", "                z = 0;"),
+    "quant_nibble_order": ("(uint32_t)q << (4 * (k % 8))", "(uint32_t)q << (4 * (7 - k % 8))"),
+    "quant_scale_from_next_column": ("S[g * N + n] = sb;", "S[g * N + (n + 1) % N] = sb;"),
 }
 
 
