@@ -81,6 +81,29 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
 w4_status w4_pack(const uint8_t *q_u4, uint32_t *Wq, int64_t K, int64_t N, void *stream);
 
 /*
+ * Round-to-nearest quantizer: produces the storage format from binary16 weights, one
+ * (scale, zero) pair per column and group of 128 along K, in the GPTQ/AWQ style the pages
+ * use for their INT4 drafts and target ("When Do Quantized Drafts Help Speculative
+ * Decoding?", "Current pilot setup"; "The Free Half of Speculative Decoding", third
+ * paragraph; neither prints the rule, so this is the plainest asymmetric reading).  Every
+ * step is binary32 with IEEE division and rint ties to even:
+ *     lo = min(0, min W), hi = max(0, max W)         over the group's 128 values
+ *     s  = binary16((hi - lo) / 15)                  (ties to even)
+ *     if s == 0 (all-zero or too narrow a range):    s = binary16(2/15), z = 8
+ *     else                                           z = clamp(rint(-lo / s), 0, 15)
+ *     q  = clamp(rint(W / s) + z, 0, 15)             (s as stored)
+ *   W_f16:      [K, N] binary16 row-major, 2-byte aligned (not modified)
+ *   Wq:         [K/8, N] uint32, 4-byte aligned, overwritten with the packed codes (as w4_pack)
+ *   scales_f16: [K/128, N] binary16, 2-byte aligned, overwritten
+ *   zeros_u4:   [K/128, N] bytes, overwritten with 0..15
+ *   K >= 128, K % 128 == 0, K/128 <= 65535, N >= 1.  Bit-exact and deterministic.  Inputs
+ *   must be finite: codes for NaN or infinite weights are unspecified (the call completes).
+ * Asynchronous on `stream`; validation errors as for w4a16_gemm.
+ */
+w4_status w4_quantize(const void *W_f16, uint32_t *Wq, void *scales_f16, uint8_t *zeros_u4, int64_t K, int64_t N,
+                      void *stream);
+
+/*
  * Streaming-read probe (a measurement aid, not part of the GEMM): reads `bytes` bytes at
  * `src` once, with the weight stream's load policy (16-byte non-temporal loads, several in
  * flight per lane), so that its rate is the achievable HBM read ceiling for a buffer of that

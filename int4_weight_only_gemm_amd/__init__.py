@@ -75,6 +75,8 @@ _lib.w4a16_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.w4a16_gemm.restype = ctypes.c_int
 _lib.w4_pack.argtypes = [_vp, _vp, _i64, _i64, _vp]
 _lib.w4_pack.restype = ctypes.c_int
+_lib.w4_quantize.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
+_lib.w4_quantize.restype = ctypes.c_int
 _lib.w4_read_probe.argtypes = [_vp, _i64, _vp, _i64, _vp]
 _lib.w4_read_probe.restype = ctypes.c_int
 _lib.w4a16_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(Plan)]
@@ -180,6 +182,28 @@ def pack(q, out=None, stream=None):
     if rc:
         raise W4Error(rc, "w4_pack")
     return out
+
+
+def quantize(W, stream=None):
+    """Round-to-nearest group-128 quantizer: float16 W [K, N] -> (Wq int32 [K/8, N],
+    scales float16 [K/128, N], zeros uint8 [K/128, N]) in the storage format."""
+    import torch
+    _check(W, "W", torch.float16, 2)
+    K, N = W.shape
+    Wq = torch.empty((K // 8, N), dtype=torch.int32, device=W.device)
+    S = torch.empty((K // 128, N), dtype=torch.float16, device=W.device)
+    Z = torch.empty((K // 128, N), dtype=torch.uint8, device=W.device)
+    rc = _lib.w4_quantize(W.data_ptr(), Wq.data_ptr(), S.data_ptr(), Z.data_ptr(), K, N, _stream_handle(stream))
+    if rc:
+        raise W4Error(rc, "w4_quantize")
+    return Wq, S, Z
+
+
+def quantize_raw(W_ptr: int, Wq_ptr: int, S_ptr: int, Z_ptr: int, K: int, N: int, stream_handle: int = 0) -> None:
+    """Direct C-ABI call of the quantizer on raw device pointers."""
+    rc = _lib.w4_quantize(W_ptr, Wq_ptr, S_ptr, Z_ptr, K, N, stream_handle)
+    if rc:
+        raise W4Error(rc, "w4_quantize")
 
 
 def read_probe(buf, blocks: int = 768, out=None, stream=None):

@@ -788,6 +788,100 @@ __global__ __launch_bounds__(256) void w4_pack_kernel(const uint8_t *__restrict_
     }
 }
 
+// Round-to-nearest quantizer: the producer of the storage format.  For each column and
+// group of 128 along K (the GPTQ/AWQ-style INT4 format the pages use for their drafts and
+// targets, "When Do Quantized Drafts Help Speculative Decoding?", "Current pilot setup";
+// "The Free Half of Speculative Decoding", third paragraph), every step in binary32:
+//   lo = min(0, min W), hi = max(0, max W)     (the range holds 0, so z fits 0..15)
+//   s  = binary16((hi - lo) / 15), ties to even; an all-zero or too-narrow range (s = 0)
+//        takes s = binary16(2/15), z = 8
+//   z  = clamp(rint(-lo / s), 0, 15),  q = clamp(rint(W / s) + z, 0, 15)   (s as stored)
+// with IEEE division and rint ties to even, so the codes are reproducible bit for bit.
+// Each thread owns two adjacent columns of one group and holds both columns' 128 rows in
+// registers (one 4-byte load per row on the vector path), so every weight is read once;
+// the codes are packed 8 rows to a word as they are produced.
+__device__ __forceinline__ void quant_params(float lo, float hi, uint16_t &sbits, float &s, float &z)
+{
+    _Float16 sh = (_Float16)((hi - lo) / 15.0f);
+    s = (float)sh;
+    if (s == 0.0f) {
+        sh = (_Float16)(2.0f / 15.0f);
+        s = (float)sh;
+        z = 8.0f;
+    } else {
+        z = fminf(fmaxf(rintf(-lo / s), 0.0f), 15.0f);
+    }
+    sbits = __builtin_bit_cast(uint16_t, sh);
+}
+
+__device__ __forceinline__ uint32_t quant_code(float w, float s, float z)
+{
+    return (uint32_t)fminf(fmaxf(rintf(w / s) + z, 0.0f), 15.0f);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t *__restrict__ W, uint32_t *__restrict__ Wq,
+                                                          uint16_t *__restrict__ S, uint8_t *__restrict__ Z,
+                                                          int64_t N)
+{
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
+    if (c0 >= N) return;
+    const bool two = c0 + 1 < N;
+    const int64_t g = blockIdx.y;
+    const uint16_t *src = W + g * kGroup * N + c0;
+    uint32_t v[kGroup];  // row k: column c0 in the low half, c0 + 1 in the high half
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+        if (VEC) {
+            v[k] = *(const uint32_t *)(src + k * N);
+        } else {
+            const uint32_t a = src[k * N], b = src[k * N + (two ? 1 : 0)];  // last column: read twice
+            v[k] = a | (b << 16);
+        }
+    }
+    float lo0 = 0.0f, hi0 = 0.0f, lo1 = 0.0f, hi1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+        const f16x2 h = as_h2(v[k]);
+        lo0 = fminf(lo0, (float)h.x);
+        hi0 = fmaxf(hi0, (float)h.x);
+        lo1 = fminf(lo1, (float)h.y);
+        hi1 = fmaxf(hi1, (float)h.y);
+    }
+    uint16_t sb0, sb1;
+    float s0, z0, s1, z1;
+    quant_params(lo0, hi0, sb0, s0, z0);
+    quant_params(lo1, hi1, sb1, s1, z1);
+#pragma unroll
+    for (int kb = 0; kb < kGroup / 8; ++kb) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const f16x2 h = as_h2(v[8 * kb + j]);
+            w0 |= quant_code((float)h.x, s0, z0) << (4 * j);
+            w1 |= quant_code((float)h.y, s1, z1) << (4 * j);
+        }
+        uint32_t *dst = Wq + (g * (kGroup / 8) + kb) * N + c0;
+        if (VEC) {
+            *(u32x2 *)dst = u32x2{w0, w1};
+        } else {
+            dst[0] = w0;
+            if (two) dst[1] = w1;
+        }
+    }
+    if (VEC) {
+        *(uint32_t *)(S + g * N + c0) = (uint32_t)sb0 | ((uint32_t)sb1 << 16);
+        *(uint16_t *)(Z + g * N + c0) = (uint16_t)((uint32_t)z0 | ((uint32_t)z1 << 8));
+    } else {
+        S[g * N + c0] = sb0;
+        Z[g * N + c0] = (uint8_t)z0;
+        if (two) {
+            S[g * N + c0 + 1] = sb1;
+            Z[g * N + c0 + 1] = (uint8_t)z1;
+        }
+    }
+}
+
 // Streaming-read probe: the achievable HBM read rate for a buffer of a given size, as a
 // ceiling for the weight stream.  Each lane keeps four 16-byte non-temporal buffer loads in
 // flight (the weight stream's load policy) over a grid-stride loop and XORs what it reads;
@@ -1267,6 +1361,38 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("w4a16_gemm launch", e);
+    return W4_OK;
+}
+
+w4_status w4_quantize(const void *W_f16, uint32_t *Wq, void *scales_f16, uint8_t *zeros_u4, int64_t K, int64_t N,
+                      void *stream)
+{
+    if (!W_f16 || !Wq || !scales_f16 || !zeros_u4) {
+        set_error("w4_quantize: a required pointer is NULL");
+        return W4_ERR_NULL;
+    }
+    if (K < kGroup || K % kGroup != 0 || N < 1 || K / kGroup > 65535 || K > ((int64_t)1 << 40) / N) {
+        set_error("w4_quantize: shape K=%lld N=%lld: need K>=128, K%%128==0, K/128<=65535, N>=1",
+                  (long long)K, (long long)N);
+        return W4_ERR_SHAPE;
+    }
+    if (!aligned(W_f16, 2) || !aligned(Wq, 4) || !aligned(scales_f16, 2)) {
+        set_error("w4_quantize: W and scales must be 2-byte aligned and Wq 4-byte aligned");
+        return W4_ERR_ALIGN;
+    }
+    int dev = -1;
+    w4_status st = check_device(&dev);
+    if (st != W4_OK) return st;
+    const bool vec = N % 2 == 0 && aligned(W_f16, 4) && aligned(Wq, 8) && aligned(scales_f16, 4) && aligned(zeros_u4, 2);
+    const dim3 grid((unsigned)((N + 511) / 512), (unsigned)(K / kGroup));
+    if (vec)
+        hipLaunchKernelGGL(w4_quantize_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, (const uint16_t *)W_f16,
+                           Wq, (uint16_t *)scales_f16, zeros_u4, N);
+    else
+        hipLaunchKernelGGL(w4_quantize_kernel<false>, grid, dim3(256), 0, (hipStream_t)stream, (const uint16_t *)W_f16,
+                           Wq, (uint16_t *)scales_f16, zeros_u4, N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("w4_quantize launch", e);
     return W4_OK;
 }
 

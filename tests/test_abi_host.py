@@ -93,6 +93,20 @@ def test_kernel_choice_by_shape():
     assert w4.plan(63, 18944, 3584)["kernel"] == 3
 
 
+def test_quantize_validation():
+    lib = w4.lib()
+    qz = lib.w4_quantize
+    qz.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    assert qz(None, W16, S8, Z4, 128, 4, None) == 1
+    assert qz(A16, W16, None, Z4, 128, 4, None) == 1
+    assert qz(A16, W16, S8, Z4, 100, 4, None) == 2   # K not a multiple of 128
+    assert qz(A16, W16, S8, Z4, 128, 0, None) == 2
+    assert qz(A16, W16, S8, Z4, 128 * 65536, 1, None) == 2  # too many groups for the grid
+    assert qz(A16 + 1, W16, S8, Z4, 128, 4, None) == 3
+    assert qz(A16, W16 + 2, S8, Z4, 128, 4, None) == 3
+    assert qz(A16, W16, S8 + 1, Z4, 128, 4, None) == 3
+
+
 def test_plan_covers_shapes():
     # every shape of the synthetic workloads has a valid plan that tiles N and K exactly;
     # a balanced wide plan runs whole rounds of 256 tiles unsplit and splits the rest

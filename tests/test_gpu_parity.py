@@ -48,6 +48,83 @@ def test_read_probe_reads_every_chunk(nbytes, blocks):
     assert got == np.bitwise_xor.reduce(host[:-4])
 
 
+# ---------------------------------------------------------------- quantizer (w4_quantize)
+def _quant_weights(K, N, seed):
+    """binary16 weights with per-column magnitudes and special groups: all-zero, one-signed,
+    constant, binary16-subnormal ranges and values near the binary16 maximum."""
+    rng = np.random.default_rng(seed)
+    mag = 10.0 ** rng.uniform(-3, 2, N)
+    W = (rng.standard_normal((K, N)) * mag).astype(np.float16)
+    G = K // 128
+    for n in range(min(N, 7)):
+        g = n % G
+        rows = slice(128 * g, 128 * g + 128)
+        if n == 0:
+            W[rows, n] = 0
+        elif n == 1:
+            W[rows, n] = np.abs(W[rows, n])
+        elif n == 2:
+            W[rows, n] = -np.abs(W[rows, n])
+        elif n == 3:
+            W[rows, n] = np.float16(0.3)
+        elif n == 4:
+            W[rows, n] = (rng.standard_normal(128) * 2.0 ** -22).astype(np.float16)
+        elif n == 5:
+            W[rows, n] = (rng.uniform(-1, 1, 128) * 65504).astype(np.float16)
+        elif n == 6:
+            W[rows, n] = (rng.standard_normal(128) * 2.0 ** -16).astype(np.float16)
+    return W
+
+
+@pytest.mark.parametrize("K,N", [(128, 1), (256, 7), (384, 64), (1024, 4099), (3584, 4608), (128, 66000)])
+def test_quantize_bit_exact(orc, K, N):
+    log(f"quantize K={K} N={N}")
+    W = _quant_weights(K, N, seed=K + N)
+    Wq, S, Z = w4.quantize(torch.from_numpy(W).cuda())
+    rWq, rS, rZ = orc.quantize(W.view(np.uint16))
+    assert np.array_equal(Wq.cpu().numpy().view(np.uint32), rWq), "packed codes differ"
+    assert np.array_equal(S.cpu().numpy().view(np.uint16), rS), "scales differ"
+    assert np.array_equal(Z.cpu().numpy(), rZ), "zeros differ"
+
+
+def test_quantize_scalar_path(orc):
+    # odd N, and views whose addresses rule out the paired stores: the scalar path
+    K, N = 256, 1001
+    W = _quant_weights(K, N, seed=3)
+    dev = torch.from_numpy(W).cuda()
+    Wq, S, Z = w4.quantize(dev)
+    rWq, rS, rZ = orc.quantize(W.view(np.uint16))
+    assert np.array_equal(Wq.cpu().numpy().view(np.uint32), rWq)
+    assert np.array_equal(S.cpu().numpy().view(np.uint16), rS) and np.array_equal(Z.cpu().numpy(), rZ)
+    buf = torch.empty(K * 1000 + 1, dtype=torch.float16, device="cuda")
+    Wv = buf[1:].view(K, 1000)  # 2-byte aligned only
+    W2 = _quant_weights(K, 1000, seed=4)
+    Wv.copy_(torch.from_numpy(W2))
+    Wq2 = torch.empty((K // 8, 1000), dtype=torch.int32, device="cuda")
+    Sb = torch.empty(2 * 1000 + 1, dtype=torch.float16, device="cuda")
+    Zb = torch.empty(2 * 1000 + 1, dtype=torch.uint8, device="cuda")
+    w4.quantize_raw(Wv.data_ptr(), Wq2.data_ptr(), Sb[1:].data_ptr(), Zb[1:].data_ptr(), K, 1000,
+                    torch.cuda.current_stream().cuda_stream)
+    rWq2, rS2, rZ2 = orc.quantize(W2.view(np.uint16))
+    assert np.array_equal(Wq2.cpu().numpy().view(np.uint32), rWq2)
+    assert np.array_equal(Sb[1:].cpu().numpy().view(np.uint16).reshape(2, 1000), rS2)
+    assert np.array_equal(Zb[1:].cpu().numpy().reshape(2, 1000), rZ2)
+
+
+def test_quantize_then_gemm(orc):
+    # the producer feeds the consumer: quantize on the GPU, multiply on the GPU, and compare
+    # with the oracle's GEMM over the oracle's quantization of the same weights
+    M, K, N = 5, 3584, 4608
+    W = _quant_weights(K, N, seed=11)
+    Wq, S, Z = w4.quantize(torch.from_numpy(W).cuda())
+    x = synth.generate_custom(M, K, N, seed=12)
+    A = torch.from_numpy(x.A.view(np.int16)).cuda().view(torch.bfloat16)
+    C = w4.gemm(A, Wq, S, Z).cpu().numpy()
+    rWq, rS, rZ = orc.quantize(W.view(np.uint16))
+    Cr, Cabs = orc.gemm(x.A, rWq, rS, rZ)
+    check(C, Cr, Cabs, "quantize then gemm")
+
+
 # ------------------------------------------------------------------- tiny-shape grid
 GRID_M = [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 17, 63, 64, 65, 160]
 GRID_K = [128, 256, 384, 1152]
