@@ -852,6 +852,10 @@ __global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t *__rest
     float s0, z0, s1, z1;
     quant_params(lo0, hi0, sb0, s0, z0);
     quant_params(lo1, hi1, sb1, s1, z1);
+    // the codes convert the packed halves again: keeping 256 converted values from the
+    // range pass alive would double the registers (and cost two thirds of the occupancy)
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) asm volatile("" : "+v"(v[k]));
 #pragma unroll
     for (int kb = 0; kb < kGroup / 8; ++kb) {
         uint32_t w0 = 0, w1 = 0;
