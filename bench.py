@@ -80,6 +80,8 @@ def parse():
                          "(e.g. 512 copies of the single GEMM exceed the on-chip caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--op", choices=("gemm", "quantize"), default="gemm",
+                    help="gemm: the W4A16 step (default); quantize: w4_quantize over the step's weight matrices")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of graph replays")
     ap.add_argument("--eager-steps", type=int, default=0,
                     help="only run this many eager steps (for a profiler) and print nothing else")
@@ -114,6 +116,8 @@ def main():
         return
 
     wl = synth.with_copies(synth.WORKLOADS[args.workload], args.copies)
+    if args.op == "quantize":
+        return bench_quantize(args, wl, dev)
     t0 = time.time()
     gemms = []  # (spec, device tensors, out)
     host_sample = []
@@ -319,6 +323,102 @@ def main():
         },
         "cpu_baseline": cpu,
         "ceiling": ceiling,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_quantize(args, wl, dev):
+    """w4_quantize over every weight matrix of the workload (binary16 weights drawn on the
+    device, N(0, 0.02^2) with a per-matrix seed), captured in a HIP graph like the GEMM step.
+    Bytes moved per weight: 2 (binary16 read) + 0.5234375 (storage format written)."""
+    import torch
+    import int4_weight_only_gemm_amd as w4
+
+    t0 = time.time()
+    mats = []
+    for spec in wl.gemms:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(int(np.random.SeedSequence(list(spec.seed) + [2]).generate_state(1)[0]))
+        W = torch.randn((spec.K, spec.N), dtype=torch.float16, device=dev, generator=gen) * 0.02
+        outs = (torch.empty((spec.K // 8, spec.N), dtype=torch.int32, device=dev),
+                torch.empty((spec.K // 128, spec.N), dtype=torch.float16, device=dev),
+                torch.empty((spec.K // 128, spec.N), dtype=torch.uint8, device=dev))
+        mats.append((spec, W, outs))
+    torch.cuda.synchronize()
+    nbytes = sum(spec.K * spec.N * 2 + spec.weight_bytes for spec, _, _ in mats)
+    log(f"{args.workload}: {len(mats)} weight matrices, {nbytes / 1e9:.3f} GB moved per step, "
+        f"inputs ready in {time.time() - t0:.1f} s")
+    stream = torch.cuda.Stream(device=dev)
+    handle = stream.cuda_stream
+
+    def step():
+        for spec, W, (Wq, S, Z) in mats:
+            w4.quantize_raw(W.data_ptr(), Wq.data_ptr(), S.data_ptr(), Z.data_ptr(), spec.K, spec.N, handle)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            graph.replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        ev0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    launches = args.steps * len(mats)
+    avg_us = ev0.elapsed_time(ev1) * 1e3 / launches
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step, {gbs:.1f} GB/s, avg launch {avg_us:.2f} us")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle's quantizer on the host, over the step's matrices in order (wrapping
+        # round), on host copies of the same weights, until CPU_SAMPLE_SECONDS have passed
+        import oracle
+        orc = oracle.get()
+        sample = mats[:min(len(mats), 8)]  # the first layers' matrices, copied before timing
+        host = [(spec, W.cpu().numpy().view(np.uint16)) for spec, W, _ in sample]
+        t1 = time.perf_counter()
+        done, moved = 0, 0
+        while time.perf_counter() - t1 < CPU_SAMPLE_SECONDS:
+            spec, Wh = host[done % len(host)]
+            orc.quantize(Wh)
+            moved += spec.K * spec.N * 2 + spec.weight_bytes
+            done += 1
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{done} quantizations of the first {len(host)} weight matrices of {args.workload}, "
+                         f"wrapping round (single-threaded oracle quantizer), {moved / 1e6:.1f} MB moved in {dt:.2f} s"}
+        log(f"cpu oracle quantizer: {cpu['value']} GB/s")
+
+    out = {
+        "metric": "w4_quantize GB/s (binary16 weights read + storage format written)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "op": "quantize", "matrices_per_step": len(mats),
+                   "bytes_per_step": nbytes, "hip_graph": True},
+        "roofline": {"bound": "hbm", "kernel": "w4_quantize_kernel", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(avg_us, 3), "launches_timed": launches},
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
