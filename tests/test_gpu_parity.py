@@ -337,6 +337,40 @@ def test_back_to_back_shapes_reproducible(orc):
         check(C.cpu().numpy()[:, cols], Cr, Cabs, f"b2b {M}x{K}x{N}")
 
 
+def test_concurrent_streams_and_threads():
+    # split-K plans keep a workspace (partials and arrival counters) per stream: calls on
+    # two streams, issued from two host threads with no synchronization between them, must
+    # give the single-stream results bit for bit
+    import threading
+    shapes = [(5, 3584, 4608), (5, 18944, 3584), (5, 3584, 37888), (160, 4096, 4096)]
+    xs = [to_dev(synth.generate_custom(M, K, N, seed=51)) for (M, K, N) in shapes]
+    ref = [run(d).clone() for d in xs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty_like(r) for r in ref] for _ in streams]
+    errors = []
+
+    def worker(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for rep in range(20):
+                    for j in (range(len(xs)) if i == 0 else reversed(range(len(xs)))):
+                        run(xs[j], out=outs[i][j])
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        for j, r in enumerate(ref):
+            assert torch.equal(outs[i][j], r), f"stream {i} shape {shapes[j]} differs"
+
+
 def test_graph_replay_matches_eager():
     # tall split plans, and balanced wide plans (unsplit tiles plus split tiles)
     shapes = [(5, 3584, 4608), (5, 18944, 3584), (1, 1536, 17920), (5, 3584, 37888)]
