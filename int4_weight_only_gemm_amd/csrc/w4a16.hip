@@ -796,7 +796,9 @@ __global__ __launch_bounds__(256) void w4_pack_kernel(const uint8_t *__restrict_
 //   s  = binary16((hi - lo) / 15), ties to even; an all-zero or too-narrow range (s = 0)
 //        takes s = binary16(2/15), z = 8
 //   z  = clamp(rint(-lo / s), 0, 15),  q = clamp(rint(W / s) + z, 0, 15)   (s as stored)
-// with IEEE division and rint ties to even, so the codes are reproducible bit for bit.
+// with IEEE division and rint ties to even, so the codes are reproducible bit for bit (the
+// kernel divides by multiplying with the reciprocal where that provably gives the same
+// integer, see quant_rint_div).
 // Each thread owns two adjacent columns of one group and holds both columns' 128 rows in
 // registers (one 4-byte load per row on the vector path), so every weight is read once;
 // the codes are packed 8 rows to a word as they are produced.
@@ -814,9 +816,23 @@ __device__ __forceinline__ void quant_params(float lo, float hi, uint16_t &sbits
     sbits = __builtin_bit_cast(uint16_t, sh);
 }
 
-__device__ __forceinline__ uint32_t quant_code(float w, float s, float z)
+// rint(w / s) with IEEE division, computed as rint(w * r), r = 1/s correctly rounded: for
+// |w / s| < 16 the product is within 2^-19 of the exact quotient and the correctly rounded
+// quotient within 2^-20, so both round to the same integer unless the quotient lies within
+// 2^-16 of a half-integer; those rare elements take the IEEE division (a branch that waves
+// skip when none of their lanes needs it).  |w / s| <= 15 up to rounding here, since the
+// grid spans the group's range.
+__device__ __forceinline__ float quant_rint_div(float w, float s, float r)
 {
-    return (uint32_t)fminf(fmaxf(rintf(w / s) + z, 0.0f), 15.0f);
+    const float u = w * r;
+    float q = rintf(u);
+    if (__builtin_expect(fabsf(u - (floorf(u) + 0.5f)) < 0x1p-16f, 0)) q = rintf(w / s);
+    return q;
+}
+
+__device__ __forceinline__ uint32_t quant_code(float w, float s, float r, float z)
+{
+    return (uint32_t)fminf(fmaxf(quant_rint_div(w, s, r) + z, 0.0f), 15.0f);
 }
 
 template <bool VEC>
@@ -852,6 +868,7 @@ __global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t *__rest
     float s0, z0, s1, z1;
     quant_params(lo0, hi0, sb0, s0, z0);
     quant_params(lo1, hi1, sb1, s1, z1);
+    const float r0 = 1.0f / s0, r1 = 1.0f / s1;
     // the codes convert the packed halves again: keeping 256 converted values from the
     // range pass alive would double the registers (and cost two thirds of the occupancy)
 #pragma unroll
@@ -862,8 +879,8 @@ __global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t *__rest
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const f16x2 h = as_h2(v[8 * kb + j]);
-            w0 |= quant_code((float)h.x, s0, z0) << (4 * j);
-            w1 |= quant_code((float)h.y, s1, z1) << (4 * j);
+            w0 |= quant_code((float)h.x, s0, r0, z0) << (4 * j);
+            w1 |= quant_code((float)h.y, s1, r1, z1) << (4 * j);
         }
         uint32_t *dst = Wq + (g * (kGroup / 8) + kb) * N + c0;
         if (VEC) {

@@ -87,6 +87,25 @@ def test_quantize_bit_exact(orc, K, N):
     assert np.array_equal(Z.cpu().numpy(), rZ), "zeros differ"
 
 
+def test_quantize_ties_and_near_ties(orc):
+    # weights at and next to grid midpoints: the kernel's reciprocal shortcut must hand
+    # these to the IEEE division and round ties to even, exactly as the oracle does
+    rng = np.random.default_rng(61)
+    cols = []
+    for s, z in [(0.5, 6), (0.125, 0), (3 * 2.0 ** -6, 8), (1.25, 3), (2.0 ** -10, 15), (0.75, 9), (5.0, 7)]:
+        mid = (np.arange(15) - z + 0.5) * s
+        ulp = np.spacing(np.abs(mid).astype(np.float16)).astype(np.float64)
+        near = np.r_[mid, mid + ulp, mid - ulp]
+        g = np.r_[-z * s, (15 - z) * s, rng.choice(near, 126)]
+        cols.append(g)
+    W = np.stack(cols, 1).astype(np.float16)
+    W = np.concatenate([W, W[::-1]], 0)  # two groups
+    Wq, S, Z = w4.quantize(torch.from_numpy(W).cuda())
+    rWq, rS, rZ = orc.quantize(W.view(np.uint16))
+    assert np.array_equal(Wq.cpu().numpy().view(np.uint32), rWq), "codes differ at or near ties"
+    assert np.array_equal(S.cpu().numpy().view(np.uint16), rS) and np.array_equal(Z.cpu().numpy(), rZ)
+
+
 def test_quantize_scalar_path(orc):
     # odd N, and views whose addresses rule out the paired stores: the scalar path
     K, N = 256, 1001
