@@ -1,6 +1,6 @@
-"""The oracle: a plain fp64 CPU reference for the W4A16 GEMM, its packing rule, and the
-round-to-nearest quantizer that produces the format (binary32, as the pages' format is
-produced; see the C source).
+"""The oracle: a plain fp64 CPU reference for the W4A16 GEMM and its 8-bit variant (W8A16),
+their packing rules, and the round-to-nearest quantizer that produces the 4-bit format
+(binary32, as the pages' format is produced; see the C source).
 
 TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check in __graft_entry__ and the
 bench's CPU-baseline leg may import this package. It shares no code with the HIP
@@ -69,6 +69,12 @@ class Oracle:
         lib.oracle_f32_to_f16.restype = ctypes.c_uint16
         lib.oracle_w4_quantize.argtypes = [vp, vp, vp, vp, i64, i64]
         lib.oracle_w4_quantize.restype = ctypes.c_int
+        lib.oracle_w8a16_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, ctypes.c_int]
+        lib.oracle_w8a16_gemm.restype = ctypes.c_int
+        lib.oracle_w8_pack.argtypes = [vp, vp, i64, i64]
+        lib.oracle_w8_pack.restype = ctypes.c_int
+        lib.oracle_w8_unpack.argtypes = [vp, vp, i64, i64]
+        lib.oracle_w8_unpack.restype = ctypes.c_int
         self._lib = lib
 
     # -- decoders -----------------------------------------------------------------
@@ -124,21 +130,44 @@ class Oracle:
             raise ValueError(f"oracle unpack rejected shape {Wq.shape}")
         return out
 
+    def pack8(self, q: np.ndarray) -> np.ndarray:
+        """8-bit codes uint8 [K, N] -> uint32 [K/4, N] (byte j of a word holds k = 4 kb + j)."""
+        q = np.ascontiguousarray(q, dtype=np.uint8)
+        K, N = q.shape
+        out = np.empty((K // 4, N), dtype=np.uint32)
+        rc = self._lib.oracle_w8_pack(_ptr(q), _ptr(out), K, N)
+        if rc:
+            raise ValueError(f"oracle pack8 rejected shape {q.shape}")
+        return out
+
+    def unpack8(self, Wq8: np.ndarray) -> np.ndarray:
+        Wq8 = np.ascontiguousarray(Wq8, dtype=np.uint32)
+        KB, N = Wq8.shape
+        out = np.empty((KB * 4, N), dtype=np.uint8)
+        rc = self._lib.oracle_w8_unpack(_ptr(Wq8), _ptr(out), KB * 4, N)
+        if rc:
+            raise ValueError(f"oracle unpack8 rejected shape {Wq8.shape}")
+        return out
+
     # -- the GEMM -----------------------------------------------------------------
     def gemm(self, A: np.ndarray, Wq: np.ndarray, S: np.ndarray, Z: np.ndarray,
-             cols: Optional[np.ndarray] = None, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+             cols: Optional[np.ndarray] = None, threads: int = 0, bits: int = 4) -> Tuple[np.ndarray, np.ndarray]:
         """Return (C, Cabs), both float64 [M, ncols]: C = A.W and Cabs = sum_k |A.W| terms.
 
-        A: uint16 bf16 bits [M,K]; Wq: uint32 [K/8,N]; S: uint16 fp16 bits [K/128,N];
-        Z: uint8 [K/128,N]; cols: optional int64 column indices.
+        A: uint16 bf16 bits [M,K]; Wq: uint32 [K*bits/32,N] (bits = 4: 8 codes per word,
+        zeros' low nibble; bits = 8: 4 codes per word, full-byte zeros); S: uint16 fp16 bits
+        [K/128,N]; Z: uint8 [K/128,N]; cols: optional int64 column indices.
         """
+        if bits not in (4, 8):
+            raise ValueError("bits must be 4 or 8")
+        per_word = 32 // bits
         A = np.ascontiguousarray(A, dtype=np.uint16)
         Wq = np.ascontiguousarray(Wq, dtype=np.uint32)
         S = np.ascontiguousarray(S, dtype=np.uint16)
         Z = np.ascontiguousarray(Z, dtype=np.uint8)
         M, K = A.shape
         KB, N = Wq.shape
-        if KB * 8 != K or S.shape != (K // 128, N) or Z.shape != (K // 128, N):
+        if KB * per_word != K or S.shape != (K // 128, N) or Z.shape != (K // 128, N):
             raise ValueError("inconsistent shapes")
         if cols is not None:
             cols = np.ascontiguousarray(cols, dtype=np.int64)
@@ -147,8 +176,8 @@ class Oracle:
             nc = N
         C = np.empty((M, nc), dtype=np.float64)
         Cabs = np.empty((M, nc), dtype=np.float64)
-        rc = self._lib.oracle_w4a16_gemm(_ptr(A), _ptr(Wq), _ptr(S), _ptr(Z), M, K, N,
-                                         _ptr(cols), nc, _ptr(C), _ptr(Cabs), int(threads))
+        fn = self._lib.oracle_w4a16_gemm if bits == 4 else self._lib.oracle_w8a16_gemm
+        rc = fn(_ptr(A), _ptr(Wq), _ptr(S), _ptr(Z), M, K, N, _ptr(cols), nc, _ptr(C), _ptr(Cabs), int(threads))
         if rc:
             raise ValueError(f"oracle rejected the shape M={M} K={K} N={N} (rc={rc})")
         return C, Cabs

@@ -2,7 +2,8 @@
  * w4a16_oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
  * The plain, slow, obviously correct CPU reference for the group-wise INT4
- * weight-only GEMM (W4A16).  Only the tests, the smoke check and the bench's CPU
+ * weight-only GEMM (W4A16), its 8-bit variant (W8A16, further down) and the 4-bit
+ * quantizer.  Only the tests, the smoke check and the bench's CPU
  * baseline leg load it; the product path never does.  It shares no source, header,
  * table or helper with the HIP library.
  *
@@ -177,6 +178,109 @@ int oracle_w4_unpack(const uint32_t *Wq, uint8_t *q, int64_t K, int64_t N)
     if (K < 8 || K % 8 != 0 || N < 1) return -1;
     for (int64_t k = 0; k < K; ++k)
         for (int64_t n = 0; n < N; ++n) q[k * N + n] = (uint8_t)oracle_code(Wq, N, k, n);
+    return 0;
+}
+
+/*
+ * The 8-bit variant (W8A16).  "When Do Quantized Drafts Help Speculative Decoding?",
+ * "Current pilot setup" and "Results": the pilot runs a GPTQ INT8 draft beside the GPTQ
+ * INT4 one, through the same weight-only path.  The same group-wise asymmetric reading,
+ * with 8-bit codes and 8-bit zero points:
+ *
+ *   W[k,n] = (q[k,n] - z[g,n]) * s[g,n],      q, z in 0..255,  g = floor(k / 128)
+ *
+ *   Wq8 uint32 [K/4,N] row-major; byte j (bits 8j..8j+7) of Wq8[kb,n] is q[4kb+j, n]
+ *   s   IEEE binary16 [K/128,N]
+ *   z   one byte per entry [K/128,N]; all eight bits are the zero point
+ *
+ * Every term A*(q-z)*s is exact in binary64 (8 + 9 + 11 significant bits); the sums run
+ * in plain k order, as in the 4-bit GEMM above.
+ */
+static inline int oracle_byte_code(const uint32_t *Wq8, int64_t N, int64_t k, int64_t n)
+{
+    uint32_t word = Wq8[(k / 4) * N + n];
+    return (int)((word >> (8 * (k % 4))) & 0xFFu);
+}
+
+int oracle_w8a16_gemm(const uint16_t *A, const uint32_t *Wq8, const uint16_t *S,
+                      const uint8_t *Z, int64_t M, int64_t K, int64_t N,
+                      const int64_t *cols, int64_t ncols, double *C, double *Cabs,
+                      int nthreads)
+{
+    if (M < 1 || N < 1 || K < ORACLE_GROUP || K % ORACLE_GROUP != 0) return -1;
+    if (!cols) ncols = N;
+    if (ncols < 1) return -1;
+    for (int64_t c = 0; cols && c < ncols; ++c)
+        if (cols[c] < 0 || cols[c] >= N) return -1;
+
+    double *Ak = (double *)malloc(sizeof(double) * (size_t)M * (size_t)K);
+    if (!Ak) return -2;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) Ak[k * M + m] = oracle_bf16_to_f64(A[m * K + k]);
+
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *sum = (double *)malloc(sizeof(double) * (size_t)M * 2);
+        if (!sum) {
+#pragma omp atomic write
+            failed = 1;
+        }
+        double *abs_sum = sum ? sum + M : NULL;
+#pragma omp for schedule(static)
+        for (int64_t c = 0; c < ncols; ++c) {
+            if (!sum) continue;
+            int64_t n = cols ? cols[c] : c;
+            for (int64_t m = 0; m < M; ++m) { sum[m] = 0.0; abs_sum[m] = 0.0; }
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t grp = k / ORACLE_GROUP;
+                int zp = Z[grp * N + n];
+                double sc = oracle_f16_to_f64(S[grp * N + n]);
+                int diff = oracle_byte_code(Wq8, N, k, n) - zp;
+                double wv = (double)diff * sc;          /* exact: 9 x 11 bits */
+                const double *a = Ak + k * M;
+                for (int64_t m = 0; m < M; ++m) {
+                    double term = a[m] * wv;            /* exact: 8 x 20 bits */
+                    sum[m] += term;
+                    abs_sum[m] += fabs(term);
+                }
+            }
+            for (int64_t m = 0; m < M; ++m) {
+                C[m * ncols + c] = sum[m];
+                if (Cabs) Cabs[m * ncols + c] = abs_sum[m];
+            }
+        }
+        free(sum);
+    }
+    free(Ak);
+    return failed ? -2 : 0;
+}
+
+/* Packing rule of the 8-bit format: Wq8[kb,n] = sum_j q[4kb+j,n] << 8j. */
+int oracle_w8_pack(const uint8_t *q, uint32_t *Wq8, int64_t K, int64_t N)
+{
+    if (K < 4 || K % 4 != 0 || N < 1) return -1;
+    for (int64_t kb = 0; kb < K / 4; ++kb)
+        for (int64_t n = 0; n < N; ++n) {
+            uint32_t word = 0;
+            for (int j = 0; j < 4; ++j)
+                word |= (uint32_t)q[(4 * kb + j) * N + n] << (8 * j);
+            Wq8[kb * N + n] = word;
+        }
+    return 0;
+}
+
+/* Inverse of the 8-bit packing rule: q[k,n] = byte (k mod 4) of Wq8[k/4, n]. */
+int oracle_w8_unpack(const uint32_t *Wq8, uint8_t *q, int64_t K, int64_t N)
+{
+    if (K < 4 || K % 4 != 0 || N < 1) return -1;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) q[k * N + n] = (uint8_t)oracle_byte_code(Wq8, N, k, n);
     return 0;
 }
 

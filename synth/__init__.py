@@ -22,6 +22,10 @@ Value recipe (the pages give no distribution; these are the stated synthetic inp
        directly, whose 8 nibbles are then i.i.d. uniform 0..15
   s  = |N(0, 1)| * 0.02 + 1e-3 computed in float64, rounded to float16 (RNE)
   z  ~ uniform integers 0..15, one byte each
+8-bit weights (the GPTQ INT8 draft of "When Do Quantized Drafts Help Speculative Decoding?",
+"Current pilot setup"): q and z uniform 0..255 (words: 4 i.i.d. uniform bytes), and the
+4-bit scale recipe divided by 16, s = (|N(0, 1)| * 0.02 + 1e-3) / 16, so that the dequantized
+weights span the same range as the 4-bit ones.
 Every (layer, projection) gets its own PCG64 stream spawned from
 SeedSequence([0, workload_id, layer, projection_index]) so any single GEMM can be
 regenerated without drawing the others.
@@ -68,13 +72,14 @@ class GemmSpec:
     N: int
     seed: Tuple[int, ...]  # SeedSequence entropy for this GEMM's draws
     q_as_bytes: bool = False  # draw unpacked u8 codes (packed later by the pack entry point)
+    bits: int = 4             # code width: 4 (W4A16) or 8 (W8A16)
 
     @property
     def weight_bytes(self) -> int:
         """Bytes of the quantized weight as stored at the boundary:
-        K*N/2 (nibbles) + 2*K*N/128 (fp16 scales) + K*N/128 (u8 zeros)."""
+        K*N*bits/8 (codes) + 2*K*N/128 (fp16 scales) + K*N/128 (u8 zeros)."""
         g = self.K // GROUP
-        return self.K * self.N // 2 + 2 * g * self.N + g * self.N
+        return self.K * self.N * self.bits // 8 + 2 * g * self.N + g * self.N
 
     @property
     def flops(self) -> int:
@@ -96,12 +101,12 @@ class Workload:
         return sum(g.flops for g in self.gemms)
 
 
-def _model_pass(wid: int, model: str, M: int, layers: int) -> Tuple[GemmSpec, ...]:
+def _model_pass(wid: int, model: str, M: int, layers: int, bits: int = 4) -> Tuple[GemmSpec, ...]:
     out = []
     for layer in range(layers):
         for pi, proj in enumerate(PROJ_ORDER):
             K, N = MODEL_SHAPES[model][proj]
-            out.append(GemmSpec(f"L{layer}.{proj}", M, K, N, (0, wid, layer, pi)))
+            out.append(GemmSpec(f"L{layer}.{proj}", M, K, N, (0, wid, layer, pi), bits=bits))
     return tuple(out)
 
 
@@ -128,6 +133,12 @@ WORKLOADS: Dict[str, Workload] = {
             "qwen2.5-1.5b-draft-m1",
             "draft step of a Qwen2.5-1.5B-shaped model, M=1, 28 layers x {qkv,o,gate_up,down}",
             _model_pass(2, "qwen2.5-1.5b", 1, 28),
+        ),
+        Workload(
+            "qwen2.5-1.5b-draft-m1-w8",
+            "draft step of a Qwen2.5-1.5B-shaped model with 8-bit weights (W8A16), M=1, "
+            "28 layers x {qkv,o,gate_up,down}",
+            _model_pass(8, "qwen2.5-1.5b", 1, 28, bits=8),
         ),
         Workload(
             "qwen2.5-7b-verify-m5",
@@ -185,10 +196,10 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 class GemmInputs:
     """Host arrays in the boundary's storage formats (all C-contiguous)."""
     A: np.ndarray      # uint16 [M, K]   bfloat16 bit patterns, row-major
-    Wq: np.ndarray     # uint32 [K/8, N] packed codes (None if only q was drawn)
+    Wq: np.ndarray     # uint32 [K*bits/32, N] packed codes (None if only q was drawn)
     q: Optional[np.ndarray]  # uint8 [K, N] unpacked codes, when drawn as bytes
     S: np.ndarray      # uint16 [K/128, N] float16 bit patterns
-    Z: np.ndarray      # uint8 [K/128, N]  zero points (low nibble used)
+    Z: np.ndarray      # uint8 [K/128, N]  zero points (4-bit: low nibble used)
 
 
 def _rng(seed: Tuple[int, ...]) -> np.random.Generator:
@@ -199,21 +210,23 @@ def draw_activations(rng: np.random.Generator, M: int, K: int) -> np.ndarray:
     return f32_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
 
 
-def draw_scales(rng: np.random.Generator, G: int, N: int) -> np.ndarray:
+def draw_scales(rng: np.random.Generator, G: int, N: int, bits: int = 4) -> np.ndarray:
     s = np.abs(rng.standard_normal((G, N))) * 0.02 + 1e-3
+    if bits == 8:
+        s = s / 16.0
     return s.astype(np.float16).view(np.uint16)
 
 
-def draw_zeros(rng: np.random.Generator, G: int, N: int) -> np.ndarray:
-    return rng.integers(0, 16, size=(G, N), dtype=np.uint8)
+def draw_zeros(rng: np.random.Generator, G: int, N: int, bits: int = 4) -> np.ndarray:
+    return rng.integers(0, 1 << bits, size=(G, N), dtype=np.uint8)
 
 
-def draw_codes(rng: np.random.Generator, K: int, N: int) -> np.ndarray:
-    return rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+def draw_codes(rng: np.random.Generator, K: int, N: int, bits: int = 4) -> np.ndarray:
+    return rng.integers(0, 1 << bits, size=(K, N), dtype=np.uint8)
 
 
-def draw_words(rng: np.random.Generator, K: int, N: int) -> np.ndarray:
-    return rng.integers(0, 1 << 32, size=(K // 8, N), dtype=np.uint32)
+def draw_words(rng: np.random.Generator, K: int, N: int, bits: int = 4) -> np.ndarray:
+    return rng.integers(0, 1 << 32, size=(K * bits // 32, N), dtype=np.uint32)
 
 
 def generate(spec: GemmSpec) -> GemmInputs:
@@ -222,28 +235,31 @@ def generate(spec: GemmSpec) -> GemmInputs:
     M, K, N = spec.M, spec.K, spec.N
     if K % GROUP:
         raise ValueError("K must be a multiple of 128")
+    if spec.bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
     G = K // GROUP
     wseed = spec.seed[:4]  # weight stream: shared by every M of a gamma-sweep copy
     wr = _rng(wseed + (1,))
     if spec.q_as_bytes:
-        q = draw_codes(wr, K, N)
+        q = draw_codes(wr, K, N, spec.bits)
         Wq = None
     else:
         q = None
-        Wq = draw_words(wr, K, N)
-    S = draw_scales(wr, G, N)
-    Z = draw_zeros(wr, G, N)
+        Wq = draw_words(wr, K, N, spec.bits)
+    S = draw_scales(wr, G, N, spec.bits)
+    Z = draw_zeros(wr, G, N, spec.bits)
     ar = _rng(tuple(spec.seed) + (0,))
     A = draw_activations(ar, M, K)
     return GemmInputs(A=A, Wq=Wq, q=q, S=S, Z=Z)
 
 
 def generate_custom(M: int, K: int, N: int, seed: int, q_as_bytes: bool = False,
-                    z_range: Tuple[int, int] = (0, 16)) -> GemmInputs:
+                    z_range: Optional[Tuple[int, int]] = None, bits: int = 4) -> GemmInputs:
     """Inputs for an arbitrary shape (parity grids, edge cases) with the standard recipe."""
-    spec = GemmSpec("custom", M, K, N, (0, 99, seed, M * 1_000_003 + K * 1009 + N), q_as_bytes)
+    spec = GemmSpec("custom", M, K, N, (0, 99 + (bits == 8), seed, M * 1_000_003 + K * 1009 + N), q_as_bytes,
+                    bits=bits)
     x = generate(spec)
-    if z_range != (0, 16):
+    if z_range is not None and z_range != (0, 1 << bits):
         r = _rng((0, 98, seed))
         x.Z = r.integers(z_range[0], z_range[1], size=x.Z.shape, dtype=np.uint8)
     return x

@@ -21,7 +21,12 @@ What pins what:
     value, every midpoint and random values;
   * the quantizer: values on the grid (exact scales, zeros and codes), ties at grid
     midpoints (to even), all-zero and one-signed groups, the half-step error bound and the
-    scale's agreement with the range, power-of-two scaling, column and group permutations.
+    scale's agreement with the range, power-of-two scaling, column and group permutations;
+  * the 8-bit variant: hand-worked words (tests/golden/pack8_words.txt) and closed forms
+    (tests/golden/closed_forms8.txt), round trips against numpy's byte view of the words,
+    the identity and all-ones cases with zero points up to 254, one-hot rows, exact zeros,
+    exact rational brute force, a BLAS float64 matmul of the dequantized W, column sampling,
+    thread count and scale invariance.
 """
 from __future__ import annotations
 
@@ -457,6 +462,196 @@ def pin_quantize_layout(o):
     assert np.array_equal(S3, S[::-1]) and np.array_equal(Z3, Z[::-1]), "group order of scales/zeros"
 
 
+# ---------------------------------------------------------------------------------------
+# The 8-bit variant (W8A16): codes and zero points 0..255, 4 codes per u32 along K.
+def np_unpack8(Wq8):
+    Wq8 = np.asarray(Wq8, np.uint32)
+    KB, N = Wq8.shape
+    shifts = (8 * np.arange(4, dtype=np.uint32))[None, :, None]
+    return ((Wq8[:, None, :] >> shifts) & 0xFF).reshape(KB * 4, N).astype(np.uint8)
+
+
+def np_pack8(q):
+    # on this little-endian host the four bytes of a packed word are q[4kb..4kb+3] in order
+    q = np.ascontiguousarray(np.asarray(q, np.uint8))
+    K, N = q.shape
+    return np.ascontiguousarray(q.reshape(K // 4, 4, N).transpose(0, 2, 1)).view("<u4").reshape(K // 4, N)
+
+
+def pin_pack8_golden(o):
+    rows = []
+    with open(os.path.join(GOLDEN, "pack8_words.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                parts = line.split()
+                rows.append(([int(p) for p in parts[:4]], int(parts[4], 16)))
+    assert len(rows) >= 8
+    q = np.array([r[0] for r in rows], dtype=np.uint8).T.copy()  # [4, n]
+    words = o.pack8(q)
+    assert words.shape == (1, len(rows))
+    assert [int(w) for w in words[0]] == [r[1] for r in rows]
+    assert np.array_equal(o.unpack8(words), q)
+
+
+def pin_pack8_roundtrip(o):
+    r = np.random.default_rng(21)
+    q = r.integers(0, 256, size=(64, 23), dtype=np.uint8)
+    assert np.array_equal(o.pack8(q), np_pack8(q))
+    assert np.array_equal(o.unpack8(o.pack8(q)), q)
+    w = r.integers(0, 1 << 32, size=(16, 9), dtype=np.uint32)
+    assert np.array_equal(o.pack8(o.unpack8(w)), w)
+    assert np.array_equal(o.unpack8(w), np_unpack8(w))
+
+
+def pin_closed_forms8(o):
+    rows = []
+    with open(os.path.join(GOLDEN, "closed_forms8.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                parts = [p.strip() for p in line.split("|")]
+                rows.append((int(parts[0]), [tuple(float(v) for v in p.split()) for p in parts[1:-1]],
+                             float(parts[-1])))
+    assert len(rows) >= 4
+    for K, groups, expect in rows:
+        G = K // 128
+        assert len(groups) == G
+        N = 5
+        A = np.zeros((2, K), np.float32)
+        q = np.zeros((K, N), np.uint8)
+        S = np.zeros((G, N), np.float64)
+        Z = np.zeros((G, N), np.uint8)
+        for g, (a, qq, zz, ss) in enumerate(groups):
+            A[:, g * 128:(g + 1) * 128] = a
+            q[g * 128:(g + 1) * 128, :] = int(qq)
+            Z[g, :] = int(zz)
+            S[g, :] = ss
+        C, Cabs = o.gemm(bf16_bits(A), np_pack8(q), f16_bits(S), Z, bits=8)
+        assert np.all(C == expect), (K, groups, C, expect)
+        assert np.all(Cabs >= np.abs(C))
+
+
+def pin_identity_rowsum8(o):
+    # q = z + 1 (z up to 254) and s = 1 make W all ones: every column is the row sum of A.
+    M, K, N = 3, 384, 11
+    r = np.random.default_rng(22)
+    A = synth.f32_to_bf16_bits(r.standard_normal((M, K), dtype=np.float32))
+    Z = r.integers(0, 255, size=(K // 128, N), dtype=np.uint8)
+    Z[0, 0] = 254
+    q = np.repeat(Z + 1, 128, axis=0).astype(np.uint8)
+    S = f16_bits(np.ones((K // 128, N)))
+    C, _ = o.gemm(A, np_pack8(q), S, Z, bits=8)
+    a = np_bf16_to_f64(A)
+    for m in range(M):
+        rs = math.fsum(a[m])
+        assert np.all(np.abs(C[m] - rs) <= K * 2.0 ** -53 * np.sum(np.abs(a[m])))
+
+
+def pin_all_ones8(o):
+    # A = 1: C[m, n] = sum_g s[g,n] * (sum_{k in g} q[k,n] - 128 z[g,n]), integer inner sums.
+    M, K, N = 2, 512, 9
+    r = np.random.default_rng(23)
+    q = r.integers(0, 256, size=(K, N), dtype=np.uint8)
+    Z = r.integers(0, 256, size=(K // 128, N), dtype=np.uint8)
+    S = synth.draw_scales(r, K // 128, N, bits=8)
+    A = bf16_bits(np.ones((M, K), np.float32))
+    C, Cabs = o.gemm(A, np_pack8(q), S, Z, bits=8)
+    s = np_f16_to_f64(S)
+    for n in range(N):
+        exact = Fraction(0)
+        for g in range(K // 128):
+            isum = int(q[g * 128:(g + 1) * 128, n].astype(np.int64).sum()) - 128 * int(Z[g, n])
+            exact += Fraction(s[g, n]) * isum
+        for m in range(M):
+            assert abs(Fraction(C[m, n]) - exact) <= Fraction(K) * Fraction(2) ** -53 * Fraction(Cabs[m, n])
+
+
+def pin_one_hot8(o):
+    # A = a0 * e_{m0,k0}: row m0 of C is a0 * (q[k0,:] - z[g0,:]) * s[g0,:], exactly.
+    M, K, N = 4, 384, 21
+    x = synth.generate_custom(M, K, N, seed=24, bits=8)
+    q = np_unpack8(x.Wq)
+    s = np_f16_to_f64(x.S)
+    for (m0, k0, a0) in ((0, 0, 1.0), (1, 3, -2.5), (3, 129, 0.375), (2, 254, 96.0), (1, 383, -0.0078125)):
+        A = np.zeros((M, K), np.float32)
+        A[m0, k0] = a0
+        C, _ = o.gemm(bf16_bits(A), x.Wq, x.S, x.Z, bits=8)
+        g0 = k0 // 128
+        expect = a0 * (q[k0].astype(np.float64) - x.Z[g0]) * s[g0]
+        assert np.array_equal(C[m0], expect), (m0, k0)
+        assert np.all(C[[m for m in range(M) if m != m0]] == 0.0)
+
+
+def pin_zero_cases8(o):
+    M, K, N = 3, 256, 17
+    x = synth.generate_custom(M, K, N, seed=25, bits=8)
+    q = np.repeat(x.Z, 128, axis=0).astype(np.uint8)
+    C, Cabs = o.gemm(x.A, np_pack8(q), x.S, x.Z, bits=8)
+    assert np.all(C == 0.0) and np.all(Cabs == 0.0)
+    C, _ = o.gemm(x.A, x.Wq, np.zeros_like(x.S), x.Z, bits=8)
+    assert np.all(C == 0.0)
+
+
+def _exact_gemm8(A, Wq8, S, Z):
+    a = np_bf16_to_f64(A)
+    q = np_unpack8(Wq8).astype(np.int64)
+    s = np_f16_to_f64(S)
+    z = np.asarray(Z).astype(np.int64)
+    M, K = a.shape
+    N = q.shape[1]
+    C = [[Fraction(0)] * N for _ in range(M)]
+    B = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        for k in range(K):
+            g = k // 128
+            w = Fraction(s[g, n]) * int(q[k, n] - z[g, n])
+            for m in range(M):
+                t = Fraction(a[m, k]) * w
+                C[m][n] += t
+                B[m][n] += abs(t)
+    return C, B
+
+
+def pin_brute_force8(o):
+    for (M, K, N, seed) in ((1, 128, 3, 1), (3, 256, 5, 2), (2, 128, 4, 3)):
+        x = synth.generate_custom(M, K, N, seed=200 + seed, bits=8)
+        C, Cabs = o.gemm(x.A, x.Wq, x.S, x.Z, bits=8)
+        Ce, Be = _exact_gemm8(x.A, x.Wq, x.S, x.Z)
+        bound_scale = Fraction(K) * Fraction(2) ** -53
+        for m in range(M):
+            for n in range(N):
+                assert abs(Fraction(C[m, n]) - Ce[m][n]) <= bound_scale * Be[m][n], (M, K, N, m, n)
+                assert abs(Fraction(Cabs[m, n]) - Be[m][n]) <= bound_scale * Be[m][n], (M, K, N, m, n)
+
+
+def pin_numpy_matmul8(o):
+    # mid size: a BLAS float64 matmul of an explicitly dequantized W (numpy decoding)
+    M, K, N = 3, 1536, 2048
+    x = synth.generate_custom(M, K, N, seed=26, bits=8)
+    C, Cabs = o.gemm(x.A, x.Wq, x.S, x.Z, bits=8)
+    g = np.arange(K) // 128
+    W = (np_unpack8(x.Wq).astype(np.float64) - x.Z[g]) * np_f16_to_f64(x.S)[g]
+    Cn = np_bf16_to_f64(x.A) @ W
+    assert np.all(np.abs(Cn - C) <= 1e-12 * Cabs)
+    absn = np.abs(np_bf16_to_f64(x.A)) @ np.abs(W)
+    assert np.all(np.abs(absn - Cabs) <= 1e-12 * Cabs)
+
+
+def pin_w8_sampling_scaling_threads(o):
+    M, K, N = 4, 512, 97
+    x = synth.generate_custom(M, K, N, seed=27, bits=8)
+    C, Cabs = o.gemm(x.A, x.Wq, x.S, x.Z, bits=8)
+    C1, _ = o.gemm(x.A, x.Wq, x.S, x.Z, threads=1, bits=8)
+    assert np.array_equal(C, C1)
+    cols = np.array([96, 0, 41, 41, 7], np.int64)
+    Cs, Cabss = o.gemm(x.A, x.Wq, x.S, x.Z, cols=cols, bits=8)
+    assert np.array_equal(Cs, C[:, cols]) and np.array_equal(Cabss, Cabs[:, cols])
+    S2 = f16_bits(np_f16_to_f64(x.S) * 2.0)  # exact: the 8-bit scales are far below the fp16 maximum
+    C3, _ = o.gemm(x.A, x.Wq, S2, x.Z, bits=8)
+    assert np.array_equal(C3, 2.0 * C)
+
+
 ALL_PINS = [
     pin_f16_encoder_against_numpy,
     pin_quantize_grid_exact,
@@ -481,4 +676,14 @@ ALL_PINS = [
     pin_numpy_matmul,
     pin_power_of_two_scaling,
     pin_column_sampling_and_threads,
+    pin_pack8_golden,
+    pin_pack8_roundtrip,
+    pin_closed_forms8,
+    pin_identity_rowsum8,
+    pin_all_ones8,
+    pin_one_hot8,
+    pin_zero_cases8,
+    pin_brute_force8,
+    pin_numpy_matmul8,
+    pin_w8_sampling_scaling_threads,
 ]

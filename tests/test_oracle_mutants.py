@@ -49,6 +49,21 @@ MUTANTS = {
     "quant_degenerate_zero": ("                z = 8;", "                z = 0;"),
     "quant_nibble_order": ("(uint32_t)q << (4 * (k % 8))", "(uint32_t)q << (4 * (7 - k % 8))"),
     "quant_scale_from_next_column": ("S[g * N + n] = sb;", "S[g * N + (n + 1) % N] = sb;"),
+    # 8-bit variant
+    "w8_byte_order_reversed": ("(word >> (8 * (k % 4)))", "(word >> (8 * (3 - k % 4)))"),
+    "w8_code_masked_to_nibble": ("(8 * (k % 4))) & 0xFFu)", "(8 * (k % 4))) & 0xFu)"),
+    "w8_zero_masked_to_nibble": ("int zp = Z[grp * N + n];", "int zp = Z[grp * N + n] & 0xF;"),
+    "w8_zero_not_subtracted": ("int diff = oracle_byte_code(Wq8, N, k, n) - zp;",
+                               "int diff = oracle_byte_code(Wq8, N, k, n);"),
+    "w8_group_of_64": ("int64_t grp = k / ORACLE_GROUP;", "int64_t grp = k / 64 / 2 * 2 % (K / ORACLE_GROUP);"),
+    "w8_group_shifted": ("int64_t grp = k / ORACLE_GROUP;", "int64_t grp = ((k + 64) / ORACLE_GROUP) % (K / ORACLE_GROUP);"),
+    "w8_scale_from_next_column": ("oracle_f16_to_f64(S[grp * N + n])", "oracle_f16_to_f64(S[grp * N + (n + 1) % N])"),
+    "w8_codes_mirrored_columns": ("uint32_t word = Wq8[(k / 4) * N + n];", "uint32_t word = Wq8[(k / 4) * N + (N - 1 - n)];"),
+    "w8_word_row_off_by_one": ("uint32_t word = Wq8[(k / 4) * N + n];", "uint32_t word = Wq8[((k / 4) ^ 1) * N + n];"),
+    "w8_abs_sum_signed": ("abs_sum[m] += fabs(term);", "abs_sum[m] += term;"),
+    "w8_pack_shift_reversed": ("<< (8 * j);", "<< (8 * (3 - j));"),
+    "w8_pack_nibbles": ("word |= (uint32_t)q[(4 * kb + j) * N + n] << (8 * j);",
+                        "word |= (uint32_t)(q[(4 * kb + j) * N + n] & 0xF) << (8 * j);"),
 }
 
 
