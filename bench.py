@@ -131,7 +131,7 @@ def main():
         if x.Wq is not None:
             d["Wq"] = torch.from_numpy(x.Wq.view(np.int32)).to(dev)
         else:
-            d["Wq"] = w4.pack(torch.from_numpy(x.q).to(dev))
+            d["Wq"] = w4.pack(torch.from_numpy(x.q).to(dev), bits=spec.bits)
         d["C"] = torch.empty((spec.M, spec.N), dtype=torch.float32, device=dev)
         gemms.append((spec, d))
         if not args.no_cpu_baseline:
@@ -142,15 +142,17 @@ def main():
 
     stream = torch.cuda.Stream(device=dev)
     handle = stream.cuda_stream
-    calls = [(d["A"].data_ptr(), d["Wq"].data_ptr(), d["S"].data_ptr(), d["Z"].data_ptr(), d["C"].data_ptr(),
-              spec.M, spec.K, spec.N) for spec, d in gemms]
     lib = w4.lib()
+    # each GEMM through the C-ABI entry point of its code width
+    calls = [(lib.w8a16_gemm if spec.bits == 8 else lib.w4a16_gemm,
+              (d["A"].data_ptr(), d["Wq"].data_ptr(), d["S"].data_ptr(), d["Z"].data_ptr(), d["C"].data_ptr(),
+               spec.M, spec.K, spec.N)) for spec, d in gemms]
 
     def step():
-        for c in calls:
-            rc = lib.w4a16_gemm(*c, handle)
+        for fn, c in calls:
+            rc = fn(*c, handle)
             if rc:
-                raise w4.W4Error(rc, "w4a16_gemm")
+                raise w4.W4Error(rc, fn.__name__)
 
     # one eager step sizes the split-K workspace of this stream before capture
     with torch.cuda.stream(stream):
@@ -207,7 +209,7 @@ def main():
     # flops) per launch are the step's totals divided by the same count.
     launches = args.steps * len(calls)
     avg_dur_s = elapsed_ms * 1e-3 / launches
-    kinds = [w4.plan(spec.M, spec.K, spec.N)["kernel"] for spec, _ in gemms]
+    kinds = [w4.plan(spec.M, spec.K, spec.N, bits=spec.bits)["kernel"] for spec, _ in gemms]
     large_bytes = sum(spec.weight_bytes for (spec, _), k in zip(gemms, kinds) if k == 3)
     kernel = KERNEL_NAME_LARGE if 2 * large_bytes > wl.weight_bytes else KERNEL_NAME
     dtype = "bf16" if all(k == 3 for k in kinds) else ("f16" if all(k != 3 for k in kinds) else "f16+bf16")
@@ -276,8 +278,8 @@ def main():
         nbytes, done = 0, 0
         while time.perf_counter() - t1 < CPU_SAMPLE_SECONDS:
             spec, x = host_sample[done % len(host_sample)]
-            Wq = x.Wq if x.Wq is not None else orc.pack(x.q)
-            orc.gemm(x.A, Wq, x.S, x.Z, threads=threads)
+            Wq = x.Wq if x.Wq is not None else (orc.pack8(x.q) if spec.bits == 8 else orc.pack(x.q))
+            orc.gemm(x.A, Wq, x.S, x.Z, threads=threads, bits=spec.bits)
             nbytes += spec.weight_bytes
             done += 1
         dt = time.perf_counter() - t1

@@ -74,6 +74,30 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
                      void *stream);
 
 /*
+ * C = A . W for the 8-bit variant of the format (W8A16): the GPTQ INT8 draft that "When
+ * Do Quantized Drafts Help Speculative Decoding?" ("Current pilot setup", "Results") runs
+ * beside the INT4 one.  Same group-wise rule, W[k,n] = (q[k,n] - z[g,n]) * s[g,n], with
+ * 8-bit codes and zero points (0..255):
+ *     Wq8        [K/4, N]    uint32; byte j (bits 8j..8j+7) of Wq8[kb,n] is q[4kb+j, n]
+ *     scales_f16 [K/128, N]  IEEE binary16
+ *     zeros_u8   [K/128, N]  one byte per entry, all 8 bits are the zero point
+ *   A_bf16 and C, sizes, alignment, workspace, stream and errors as for w4a16_gemm; the
+ *   packed codes must stay below 2 GiB (K/4 * N * 4 bytes).  Every M runs on the binary16
+ *   matrix cores with the per-(row, group) power-of-two activation scaling described at
+ *   the top of this file, in row blocks of 16, so the same accuracy contract holds.
+ */
+w4_status w8a16_gemm(const void *A_bf16, const uint32_t *Wq8, const void *scales_f16,
+                     const uint8_t *zeros_u8, float *C, int64_t M, int64_t K, int64_t N,
+                     void *stream);
+
+/*
+ * Packs 8-bit codes into the 8-bit storage layout: Wq8[kb,n] = sum_j q[4kb+j,n] << 8j.
+ *   q_u8: [K, N] bytes; Wq8: [K/4, N] uint32, overwritten.
+ *   K >= 4 with K % 4 == 0, N >= 1; Wq8 must be 4-byte aligned.  Bit-exact.
+ */
+w4_status w8_pack(const uint8_t *q_u8, uint32_t *Wq8, int64_t K, int64_t N, void *stream);
+
+/*
  * Packs 4-bit codes into the storage layout: Wq[kb,n] = sum_j (q[8kb+j,n] & 0xF) << 4j.
  *   q_u4: [K, N] bytes (high nibbles ignored); Wq: [K/8, N] uint32, overwritten.
  *   K >= 8 with K % 8 == 0, N >= 1; Wq must be 4-byte aligned.  Bit-exact.
@@ -123,15 +147,16 @@ typedef struct w4_plan {
     int kernel;             /* 1 = small-M wide (4 waves per workgroup, fp16 MFMA),
                                2 = small-M tall (12 waves, fp16 MFMA),
                                3 = large-M (M >= 64, or M >= 17 with K*N >= 2^25:
-                                   8 waves, bf16 MFMA)                                       */
-    int tile_m;             /* output rows per row block (16 for kernels 1, 2; 1 to 160 for
-                               kernel 3, computed in row tiles of 32)                        */
+                                   8 waves, bf16 MFMA),
+                               4, 5 = 8-bit codes (w8a16_gemm), wide and tall as 1, 2       */
+    int tile_m;             /* output rows per row block (16 for kernels 1, 2, 4, 5; 1 to
+                               160 for kernel 3, computed in row tiles of 32)                */
     int tile_n;             /* output columns per workgroup tile (64, or 256 for kernel 3)   */
     int m_blocks;           /* row blocks of tile_m                                          */
     int n_tiles;            /* column tiles of tile_n                                        */
     int splits;             /* K splits across workgroups (1 = no workspace)                */
     int groups_per_split;   /* 128-wide K groups handled by one workgroup of a split tile    */
-    int full_tiles;         /* kernel 1: tiles 0..full_tiles-1 (row-block-major order) run
+    int full_tiles;         /* kernels 1, 4: tiles 0..full_tiles-1 (row-block-major order) run
                                unsplit, one workgroup each, and only the other tiles are
                                split (a multiple of 256: whole rounds of CUs); 0 otherwise  */
     int64_t workgroups;     /* grid size: full_tiles + (m_blocks*n_tiles - full_tiles)*splits */
@@ -139,6 +164,9 @@ typedef struct w4_plan {
 } w4_plan;
 
 w4_status w4a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out);
+
+/* How w8a16_gemm would run a shape (host only, no HIP call). */
+w4_status w8a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out);
 
 /* Static text for a status code. */
 const char *w4_status_string(w4_status s);

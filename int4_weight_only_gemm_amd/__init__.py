@@ -7,6 +7,8 @@ package fails loudly when the library has not been built (there is no fallback).
     import int4_weight_only_gemm_amd as w4
     Wq = w4.pack(q_u8)                    # [K, N] uint8 codes -> [K/8, N] int32 words
     C = w4.gemm(A_bf16, Wq, s_f16, z_u8)  # [M, N] float32
+    Wq8 = w4.pack(q_u8, bits=8)           # 8-bit codes -> [K/4, N] int32 words
+    C = w4.gemm(A_bf16, Wq8, s_f16, z_u8, bits=8)
 """
 from __future__ import annotations
 
@@ -81,6 +83,12 @@ _lib.w4_read_probe.argtypes = [_vp, _i64, _vp, _i64, _vp]
 _lib.w4_read_probe.restype = ctypes.c_int
 _lib.w4a16_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(Plan)]
 _lib.w4a16_plan.restype = ctypes.c_int
+_lib.w8a16_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+_lib.w8a16_gemm.restype = ctypes.c_int
+_lib.w8_pack.argtypes = [_vp, _vp, _i64, _i64, _vp]
+_lib.w8_pack.restype = ctypes.c_int
+_lib.w8a16_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(Plan)]
+_lib.w8a16_plan.restype = ctypes.c_int
 _lib.w4_status_string.argtypes = [ctypes.c_int]
 _lib.w4_status_string.restype = ctypes.c_char_p
 _lib.w4_last_error.argtypes = []
@@ -96,18 +104,28 @@ def header_functions(path: str = HEADER) -> List[str]:
     with open(path) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\**\s*\b(w4\w*)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\**\s*\b(w[48]\w*)\s*\(", text, flags=re.M)
 
 
 def status_string(code: int) -> str:
     return _lib.w4_status_string(code).decode()
 
 
-def plan(M: int, K: int, N: int) -> Dict[str, int]:
+def _bits_fns(bits: int):
+    if bits == 4:
+        return _lib.w4a16_gemm, "w4a16_gemm", _lib.w4_pack, "w4_pack", _lib.w4a16_plan, "w4a16_plan"
+    if bits == 8:
+        return _lib.w8a16_gemm, "w8a16_gemm", _lib.w8_pack, "w8_pack", _lib.w8a16_plan, "w8a16_plan"
+    raise ValueError("bits must be 4 or 8")
+
+
+def plan(M: int, K: int, N: int, bits: int = 4) -> Dict[str, int]:
+    """How the GEMM entry point for `bits`-wide codes would run a shape (host only)."""
+    fn, name = _bits_fns(bits)[4:]
     p = Plan()
-    rc = _lib.w4a16_plan(M, K, N, ctypes.byref(p))
+    rc = fn(M, K, N, ctypes.byref(p))
     if rc:
-        raise W4Error(rc, "w4a16_plan")
+        raise W4Error(rc, name)
     return p.as_dict()
 
 
@@ -130,12 +148,14 @@ def _check(t, name, dtype, ndim):
         raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
 
 
-def gemm(A, Wq, scales, zeros, out=None, stream=None):
+def gemm(A, Wq, scales, zeros, out=None, stream=None, bits: int = 4):
     """C[M,N] = A[M,K] . W[K,N] with W[k,n] = (q[k,n] - z[k/128,n]) * s[k/128,n].
 
-    A: bfloat16 [M,K]; Wq: int32 (or uint32) [K/8,N] packed codes; scales: float16
+    A: bfloat16 [M,K]; Wq: int32 (or uint32) [K*bits/32,N] packed codes; scales: float16
     [K/128,N]; zeros: uint8 [K/128,N]; out: optional float32 [M,N] (overwritten).
+    bits = 4 calls w4a16_gemm (zeros' low nibble), bits = 8 calls w8a16_gemm (full bytes).
     """
+    fn, name = _bits_fns(bits)[:2]
     import torch
     _check(A, "A", torch.bfloat16, 2)
     if Wq.dtype not in (torch.int32, torch.uint32):
@@ -145,7 +165,7 @@ def gemm(A, Wq, scales, zeros, out=None, stream=None):
     _check(zeros, "zeros", torch.uint8, 2)
     M, K = A.shape
     N = Wq.shape[1]
-    if Wq.shape[0] * 8 != K or scales.shape != (K // 128, N) or zeros.shape != (K // 128, N):
+    if Wq.shape[0] * (32 // bits) != K or scales.shape != (K // 128, N) or zeros.shape != (K // 128, N):
         raise ValueError(f"inconsistent shapes A{tuple(A.shape)} Wq{tuple(Wq.shape)} "
                          f"scales{tuple(scales.shape)} zeros{tuple(zeros.shape)}")
     if out is None:
@@ -154,33 +174,37 @@ def gemm(A, Wq, scales, zeros, out=None, stream=None):
         _check(out, "out", torch.float32, 2)
         if tuple(out.shape) != (M, N):
             raise ValueError("out has the wrong shape")
-    rc = _lib.w4a16_gemm(A.data_ptr(), Wq.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-                         out.data_ptr(), M, K, N, _stream_handle(stream))
+    rc = fn(A.data_ptr(), Wq.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+            out.data_ptr(), M, K, N, _stream_handle(stream))
     if rc:
-        raise W4Error(rc, "w4a16_gemm")
+        raise W4Error(rc, name)
     return out
 
 
 def gemm_raw(A_ptr: int, Wq_ptr: int, S_ptr: int, Z_ptr: int, C_ptr: int, M: int, K: int, N: int,
-             stream_handle: int = 0) -> None:
+             stream_handle: int = 0, bits: int = 4) -> None:
     """Direct C-ABI call on raw device pointers (no checks beyond the library's own)."""
-    rc = _lib.w4a16_gemm(A_ptr, Wq_ptr, S_ptr, Z_ptr, C_ptr, M, K, N, stream_handle)
+    fn, name = _bits_fns(bits)[:2]
+    rc = fn(A_ptr, Wq_ptr, S_ptr, Z_ptr, C_ptr, M, K, N, stream_handle)
     if rc:
-        raise W4Error(rc, "w4a16_gemm")
+        raise W4Error(rc, name)
 
 
-def pack(q, out=None, stream=None):
-    """Pack uint8 codes [K,N] (high nibbles ignored) into int32 words [K/8,N]."""
+def pack(q, out=None, stream=None, bits: int = 4):
+    """Pack uint8 codes [K,N] into int32 words [K*bits/32,N]: 8 codes per word for bits = 4
+    (high nibbles ignored), 4 codes per word for bits = 8."""
     import torch
+    fn, name = _bits_fns(bits)[2:4]
     _check(q, "q", torch.uint8, 2)
     K, N = q.shape
+    KB = K * bits // 32
     if out is None:
-        out = torch.empty((K // 8, N), dtype=torch.int32, device=q.device)
-    elif out.dtype not in (torch.int32, torch.uint32) or tuple(out.shape) != (K // 8, N):
-        raise ValueError("out must be int32 [K/8, N]")
-    rc = _lib.w4_pack(q.data_ptr(), out.data_ptr(), K, N, _stream_handle(stream))
+        out = torch.empty((KB, N), dtype=torch.int32, device=q.device)
+    elif out.dtype not in (torch.int32, torch.uint32) or tuple(out.shape) != (KB, N):
+        raise ValueError(f"out must be int32 [{KB}, N]")
+    rc = fn(q.data_ptr(), out.data_ptr(), K, N, _stream_handle(stream))
     if rc:
-        raise W4Error(rc, "w4_pack")
+        raise W4Error(rc, name)
     return out
 
 

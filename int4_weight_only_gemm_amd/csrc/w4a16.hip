@@ -115,6 +115,22 @@ __device__ __forceinline__ f16x8 unpack8(uint32_t w, uint32_t zlo, uint32_t zhi,
     return __builtin_bit_cast(f16x8, r);
 }
 
+// Eight 8-bit codes (two packed words, k order 0..7) -> eight exact binary16 values
+// (q_j - z), in k order.  v_perm_b32 places each code byte under the high byte 0x64 (taken
+// from `magic`, 0x64646464), which reads as the binary16 value 1024 + q; one packed add of
+// zneg = the binary16 pair of -(1024 + z) leaves q - z, exact for q, z in 0..255.
+__device__ __forceinline__ f16x8 unpack8_w8(uint32_t w0, uint32_t w1, uint32_t zneg, uint32_t magic,
+                                            uint32_t sel01, uint32_t sel23)
+{
+    const f16x2 zn = as_h2(zneg);
+    const f16x2 d0 = as_h2(__builtin_amdgcn_perm(magic, w0, sel01)) + zn;  // q0 | q1
+    const f16x2 d1 = as_h2(__builtin_amdgcn_perm(magic, w0, sel23)) + zn;  // q2 | q3
+    const f16x2 d2 = as_h2(__builtin_amdgcn_perm(magic, w1, sel01)) + zn;  // q4 | q5
+    const f16x2 d3 = as_h2(__builtin_amdgcn_perm(magic, w1, sel23)) + zn;  // q6 | q7
+    u32x4 r = {as_u(d0), as_u(d1), as_u(d2), as_u(d3)};
+    return __builtin_bit_cast(f16x8, r);
+}
+
 // Largest biased bfloat16 exponent among the 8 values of a chunk.
 __device__ __forceinline__ int chunk_max_exp(u32x4 v)
 {
@@ -143,8 +159,10 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b)
     return as_u(h);
 }
 
-// 8 bfloat16 values (k order 0..7) -> 8 binary16 values scaled by 2^x, in the same
-// element order as unpack8 (0,4,1,5,2,6,3,7).
+// 8 bfloat16 values (k order 0..7) -> 8 binary16 values scaled by 2^x, in the element
+// order of the weight operand: unpack8's (0,4,1,5,2,6,3,7) for 4-bit codes, k order for
+// 8-bit codes.
+template <int BITS>
 __device__ __forceinline__ u32x4 convert_chunk(u32x4 v, int x)
 {
     float e0 = ldexpf(__builtin_bit_cast(float, v[0] << 16), x);
@@ -155,6 +173,10 @@ __device__ __forceinline__ u32x4 convert_chunk(u32x4 v, int x)
     float e5 = ldexpf(__builtin_bit_cast(float, v[2] & 0xFFFF0000u), x);
     float e6 = ldexpf(__builtin_bit_cast(float, v[3] << 16), x);
     float e7 = ldexpf(__builtin_bit_cast(float, v[3] & 0xFFFF0000u), x);
+    if constexpr (BITS == 8) {
+        u32x4 r = {pack_h2(e0, e1), pack_h2(e2, e3), pack_h2(e4, e5), pack_h2(e6, e7)};
+        return r;
+    }
     u32x4 r = {pack_h2(e0, e4), pack_h2(e1, e5), pack_h2(e2, e6), pack_h2(e3, e7)};
     return r;
 }
@@ -169,10 +191,23 @@ __device__ __forceinline__ uint32_t xcd_local_id(uint32_t b, uint32_t n)
 }
 
 // ------------------------------------------------------------------------------------
-// Register slot of one wave for one group: 4 packed rows (one 16-byte load per lane each)
-// and the group's scales and zeros for the lane's 4 columns.
+// A group of 128 k holds 16 packed rows of 4-bit codes or 32 of 8-bit codes.  One 16-byte
+// load per lane covers 4 rows (lane quarter kq takes one), so a group takes BITS loads.
+//   4-bit: load st holds row 4 st + kq: k = 32 st + 8 kq .. + 7, one word per column.
+//   8-bit: loads 2 ks and 2 ks + 1 hold rows 8 ks + 2 kq and 8 ks + 2 kq + 1: the same
+//          k = 32 ks + 8 kq .. + 7, two words per column.
+// Either way a lane holds the 8 k of its matrix-core operand for k-step st (or ks).
+template <int BITS>
+__device__ __forceinline__ constexpr int load_row(int st)
+{
+    return BITS == 4 ? 4 * st : 8 * (st >> 1) + (st & 1);
+}
+
+// Register slot of one wave for one group: BITS loads of 4 packed rows each and the
+// group's scales and zeros for the lane's 4 columns.
+template <int BITS>
 struct GroupRegs {
-    u32x4 w[4];
+    u32x4 w[BITS];
     u32x2 s;      // 4 binary16 scales
     uint32_t z;   // 4 zero bytes
 };
@@ -196,36 +231,37 @@ struct Resources {
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords
 
-template <bool VEC>
+template <bool VEC, int BITS>
 __device__ __forceinline__ void lane_offsets(const SmallParams &p, int n0, int lane, LaneOffsets<VEC> &o)
 {
     const int c = lane & 15, kq = lane >> 4;
     const int64_t N = p.N;
     const int64_t col = n0 + 4 * c;
+    const int64_t krow = kq * (BITS / 4);  // the lane's first packed row within a load
     if (VEC) {
         const int64_t colv = col < N - 4 ? col : N - 4;  // N % 4 == 0, so N >= 4
-        o.w[0] = (uint32_t)((kq * N + colv) * 4);
+        o.w[0] = (uint32_t)((krow * N + colv) * 4);
         o.s[0] = (uint32_t)(colv * 2);
         o.z[0] = (uint32_t)colv;
     } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int64_t ct = col + t < N ? col + t : N - 1;
-            o.w[t] = (uint32_t)((kq * N + ct) * 4);
+            o.w[t] = (uint32_t)((krow * N + ct) * 4);
             o.s[t] = (uint32_t)(ct * 2);
             o.z[t] = (uint32_t)ct;
         }
     }
 }
 
-template <bool VEC>
+template <bool VEC, int BITS>
 __device__ __forceinline__ void load_group(const SmallParams &p, const Resources &rs,
-                                           const LaneOffsets<VEC> &o, int g, GroupRegs &r)
+                                           const LaneOffsets<VEC> &o, int g, GroupRegs<BITS> &r)
 {
     const uint32_t rowbytes = (uint32_t)p.N * 4;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const uint32_t so = ((uint32_t)g * 16 + 4 * st) * rowbytes;
+    for (int st = 0; st < BITS; ++st) {
+        const uint32_t so = ((uint32_t)g * (4 * BITS) + load_row<BITS>(st)) * rowbytes;
         if (VEC) {
             r.w[st] = __builtin_amdgcn_raw_buffer_load_b128(rs.W, o.w[0], so, kCacheStream);
         } else {
@@ -257,9 +293,9 @@ __device__ __forceinline__ void load_group(const SmallParams &p, const Resources
 // chunks travel in the register ring with the group's weights, so the conversion overlaps
 // the loads still in flight and there is no workgroup-wide staging phase.
 
-template <int AV>
+template <int AV, int BITS>
 struct PipeRegs {
-    u32x4 w[4];
+    u32x4 w[BITS];
     u32x2 s;      // 4 binary16 scales
     uint32_t z;   // 4 zero bytes
     u32x4 a[AV];  // activation chunks: rows 4i + lane/16, chunk lane%16 of the group
@@ -268,19 +304,19 @@ struct PipeRegs {
 constexpr int kPipeWaveBytes = kTileM * kARowBytes + kTileM * 4;  // tile + row exponents
 constexpr int kPipeExpOffset = kTileM * kARowBytes;
 
-template <bool VEC, int AV>
+template <bool VEC, int AV, int BITS>
 __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources &rs, const LaneOffsets<VEC> &o,
-                                          const uint32_t (&aoff)[AV], int g, PipeRegs<AV> &r)
+                                          const uint32_t (&aoff)[AV], int g, PipeRegs<AV, BITS> &r)
 {
     // activations first: their conversion needs only them, and can run while the
     // weights are still in flight (loads complete in issue order)
 #pragma unroll
     for (int i = 0; i < AV; ++i)
         r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[i], (uint32_t)g * (kGroup * 2), 0);
-    GroupRegs w;
-    load_group<VEC>(p, rs, o, g, w);
+    GroupRegs<BITS> w;
+    load_group<VEC, BITS>(p, rs, o, g, w);
 #pragma unroll
-    for (int st = 0; st < 4; ++st) r.w[st] = w.w[st];
+    for (int st = 0; st < BITS; ++st) r.w[st] = w.w[st];
     r.s = w.s;
     r.z = w.z;
 }
@@ -288,8 +324,8 @@ __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources 
 // Convert this wave's group of activations into its LDS tile: row r scaled by 2^x[r],
 // x[r] = 142 - (largest biased exponent of row r in the group); exponents stored next to
 // the tile.  The 16 chunks of a row sit in 16 consecutive lanes.
-template <int AV>
-__device__ __forceinline__ void stage_pipe(const PipeRegs<AV> &r, char *lds_wave, int mv, int lane)
+template <int AV, int BITS>
+__device__ __forceinline__ void stage_pipe(const PipeRegs<AV, BITS> &r, char *lds_wave, int mv, int lane)
 {
     asm volatile("" ::: "memory");  // the previous group's LDS reads stay before these writes
     const int kc = lane & 15;
@@ -298,38 +334,62 @@ __device__ __forceinline__ void stage_pipe(const PipeRegs<AV> &r, char *lds_wave
         const int row = 4 * i + (lane >> 4);
         const int e = row16_max(chunk_max_exp(r.a[i]));
         const int x = 142 - max(e, 1);
-        if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = convert_chunk(r.a[i], x);
+        if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = convert_chunk<BITS>(r.a[i], x);
         if (kc == 0) *(int *)(lds_wave + kPipeExpOffset + 4 * row) = row < mv ? x : 0;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's tile is complete
 }
 
-template <int AV>
-__device__ __forceinline__ void compute_pipe(const PipeRegs<AV> &r, const char *lds_wave, int mv, int lane,
+template <int AV, int BITS>
+__device__ __forceinline__ void compute_pipe(const PipeRegs<AV, BITS> &r, const char *lds_wave, int mv, int lane,
                                              f32x4 (&acc)[4])
 {
     const int c = lane & 15, kq = lane >> 4;
-    uint32_t magic;
-    asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
-    uint32_t zlo[4], zhi[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint32_t z = (r.z >> (8 * t)) & 0xFu;
-        zlo[t] = (0xE400u | z) * 0x00010001u;         // -(1024 + z)
-        zhi[t] = (0xD400u | (z << 4)) * 0x00010001u;  // -(64 + z)
-        asm volatile("" : "+v"(zlo[t]), "+v"(zhi[t]));
-    }
     f32x4 P[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        // rows mv..15 of the tile are zero (cleared once, never staged)
-        const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_wave + c * kARowBytes + (4 * st + kq) * 16));
+    if constexpr (BITS == 4) {
+        uint32_t magic;
+        asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+        uint32_t zlo[4], zhi[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const f16x8 b_op = unpack8(r.w[st][t], zlo[t], zhi[t], magic);
-            // the first k-step starts from a literal zero accumulator (no register clearing)
-            const f32x4 c_in = st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[t];
-            P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, c_in, 0, 0, 0);
+            const uint32_t z = (r.z >> (8 * t)) & 0xFu;
+            zlo[t] = (0xE400u | z) * 0x00010001u;         // -(1024 + z)
+            zhi[t] = (0xD400u | (z << 4)) * 0x00010001u;  // -(64 + z)
+            asm volatile("" : "+v"(zlo[t]), "+v"(zhi[t]));
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            // rows mv..15 of the tile are zero (cleared once, never staged)
+            const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_wave + c * kARowBytes + (4 * st + kq) * 16));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f16x8 b_op = unpack8(r.w[st][t], zlo[t], zhi[t], magic);
+                // the first k-step starts from a literal zero accumulator (no register clearing)
+                const f32x4 c_in = st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[t];
+                P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, c_in, 0, 0, 0);
+            }
+        }
+    } else {
+        uint32_t magic, sel01, sel23;
+        asm("v_mov_b32 %0, 0x64646464" : "=v"(magic));
+        asm("s_mov_b32 %0, 0x04010400" : "=s"(sel01));  // bytes: q0, 0x64, q1, 0x64
+        asm("s_mov_b32 %0, 0x04030402" : "=s"(sel23));  // bytes: q2, 0x64, q3, 0x64
+        uint32_t zneg[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint32_t z = (r.z >> (8 * t)) & 0xFFu;
+            zneg[t] = (0xE400u | z) * 0x00010001u;  // -(1024 + z)
+            asm volatile("" : "+v"(zneg[t]));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_wave + c * kARowBytes + (4 * ks + kq) * 16));
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f16x8 b_op = unpack8_w8(r.w[2 * ks][t], r.w[2 * ks + 1][t], zneg[t], magic, sel01, sel23);
+                const f32x4 c_in = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[t];
+                P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, c_in, 0, 0, 0);
+            }
         }
     }
     const int4 xr = *(const int4 *)(lds_wave + kPipeExpOffset + 16 * kq);
@@ -343,7 +403,7 @@ __device__ __forceinline__ void compute_pipe(const PipeRegs<AV> &r, const char *
     }
 }
 
-template <bool VEC, int WAVES, int AV, int OCC>
+template <bool VEC, int WAVES, int AV, int OCC, int BITS>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void w4a16_kernel(SmallParams p)
 {
@@ -382,12 +442,12 @@ void w4a16_kernel(SmallParams p)
     char *tile_lds = lds + wave * kPipeWaveBytes;
 
     Resources rs;
-    rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K / 8 * p.N * 4), kRsrcWord3);
+    rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K * BITS / 32 * p.N * 4), kRsrcWord3);
     rs.S = __builtin_amdgcn_make_buffer_rsrc((void *)p.S, (short)0, (int)(p.K / kGroup * p.N * 2), kRsrcWord3);
     rs.Z = __builtin_amdgcn_make_buffer_rsrc((void *)p.Z, (short)0, (int)(p.K / kGroup * p.N), kRsrcWord3);
     rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(p.M * p.K * 2), kRsrcWord3);
     LaneOffsets<VEC> lo;
-    lane_offsets<VEC>(p, n0, lane, lo);
+    lane_offsets<VEC, BITS>(p, n0, lane, lo);
     uint32_t aoff[AV];
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
@@ -408,22 +468,22 @@ void w4a16_kernel(SmallParams p)
     // Two register slots: group j+1 (weights and activations) is in flight while group j is
     // converted and computed.
     auto G = [&](int j) { return g0 + WAVES * j; };
-    auto run = [&](const PipeRegs<AV> &r) {
-        stage_pipe<AV>(r, tile_lds, mv, lane);
-        compute_pipe<AV>(r, tile_lds, mv, lane, acc);
+    auto run = [&](const PipeRegs<AV, BITS> &r) {
+        stage_pipe<AV, BITS>(r, tile_lds, mv, lane);
+        compute_pipe<AV, BITS>(r, tile_lds, mv, lane, acc);
     };
     if (n_my > 0) {
-        PipeRegs<AV> r0, r1;
-        load_pipe<VEC, AV>(p, rs, lo, aoff, G(0), r0);
+        PipeRegs<AV, BITS> r0, r1;
+        load_pipe<VEC, AV, BITS>(p, rs, lo, aoff, G(0), r0);
         int j = 0;
         for (; j + 2 < n_my; j += 2) {
-            load_pipe<VEC, AV>(p, rs, lo, aoff, G(j + 1), r1);
+            load_pipe<VEC, AV, BITS>(p, rs, lo, aoff, G(j + 1), r1);
             run(r0);
-            load_pipe<VEC, AV>(p, rs, lo, aoff, G(j + 2), r0);
+            load_pipe<VEC, AV, BITS>(p, rs, lo, aoff, G(j + 2), r0);
             run(r1);
         }
         if (j + 1 < n_my) {
-            load_pipe<VEC, AV>(p, rs, lo, aoff, G(j + 1), r1);
+            load_pipe<VEC, AV, BITS>(p, rs, lo, aoff, G(j + 1), r1);
             run(r0);
             run(r1);
         } else {
@@ -773,6 +833,22 @@ __global__ __launch_bounds__(256) void w4a16_split_reduce(const float *__restric
     }
 }
 
+// 8-bit codes: Wq8[kb,n] = sum_j q[4kb+j,n] << 8j, one word per thread.
+__global__ __launch_bounds__(256) void w8_pack_kernel(const uint8_t *__restrict__ q,
+                                                      uint32_t *__restrict__ Wq8, int64_t KB, int64_t N)
+{
+    const int64_t total = KB * N;
+    for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * 256) {
+        const int64_t kb = idx / N, n = idx - kb * N;
+        const uint8_t *src = q + (kb * 4) * N + n;
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w |= (uint32_t)src[j * N] << (8 * j);
+        Wq8[idx] = w;
+    }
+}
+
 __global__ __launch_bounds__(256) void w4_pack_kernel(const uint8_t *__restrict__ q,
                                                       uint32_t *__restrict__ Wq, int64_t KB, int64_t N)
 {
@@ -1036,7 +1112,7 @@ w4_status get_workspace(int dev, hipStream_t stream, size_t tiles, size_t part_b
     return W4_OK;
 }
 
-w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N)
+w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N, int bits = 4)
 {
     if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) {
         set_error("shape M=%lld K=%lld N=%lld: need M>=1, N>=1, K>=128, K%%128==0",
@@ -1044,7 +1120,7 @@ w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N)
         return W4_ERR_SHAPE;
     }
     // the kernels address each array with 32-bit byte offsets
-    if (K / 8 * N * 4 >= ((int64_t)1 << 31) || M * K * 2 >= ((int64_t)1 << 31)) {
+    if (K * bits / 32 * N * 4 >= ((int64_t)1 << 31) || M * K * 2 >= ((int64_t)1 << 31)) {
         set_error("shape M=%lld K=%lld N=%lld: packed weights or activations exceed 2 GiB",
                   (long long)M, (long long)K, (long long)N);
         return W4_ERR_SHAPE;
@@ -1073,7 +1149,7 @@ constexpr double kUsHandoff = 1.0;       // split-K: partial stores, arrival cou
 constexpr double kUsPerSplit = 0.4;      // ... and reading back one partial tile
 constexpr double kUsPerGroup = 0.5;      // one group per wave, per wave resident on its SIMD
 constexpr double kRowsFactor = 0.3;      // extra group cost per 4 rows beyond the first 4
-constexpr int kGroupBytes = 16 * 4 * kTileN;  // packed weights of one wave-group
+constexpr int group_bytes(int bits) { return 4 * bits * 4 * kTileN; }  // packed weights of one wave-group
 constexpr int kMinPartGroups = 4;        // balanced wide plan: groups per split part, at least
 
 struct Choice {
@@ -1082,7 +1158,7 @@ struct Choice {
     double us;
 };
 
-Choice score(const Variant &v, int64_t base, int groups, int splits, int av, int64_t K, int64_t N)
+Choice score(const Variant &v, int64_t base, int groups, int splits, int av, int64_t K, int64_t N, int bits)
 {
     Choice c = {&v, splits, 1e30};
     const int gps = (groups + splits - 1) / splits;
@@ -1094,10 +1170,10 @@ Choice score(const Variant &v, int64_t base, int groups, int splits, int av, int
     const int per_wave = (gps + v.waves - 1) / v.waves;
     const double compute = per_wave * t_group;
     const int active_waves_per_wg = gps < v.waves ? gps : v.waves;
-    const double inflight = (double)wgs * active_waves_per_wg * (per_wave < 2 ? per_wave : 2) * kGroupBytes;
+    const double inflight = (double)wgs * active_waves_per_wg * (per_wave < 2 ? per_wave : 2) * group_bytes(bits);
     double rate = inflight / (kUsLatency * 1e-6) / 1e9;  // GB/s
     if (rate > kGBsPeak) rate = kGBsPeak;
-    const double stream = (double)K * N * 0.5234375 / (rate * 1e3);  // us
+    const double stream = (double)K * N * (bits / 8.0 + 3.0 / kGroup) / (rate * 1e3);  // us
     c.us = kUsLaunch + (stream > compute ? stream : compute) +
            (splits > 1 ? kUsHandoff + kUsPerSplit * splits : 0.0);
     return c;
@@ -1179,7 +1255,10 @@ void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->workspace_bytes = best_s > 1 ? best_s * ((M * N + 3) / 4 * 4) * 4 : 0;
 }
 
-void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
+// Kernel ids of the small-M shapes: 1 / 2 (4-bit codes, wide / tall), 4 / 5 (8-bit codes).
+int small_kernel_id(bool tall, int bits) { return (bits == 8 ? 3 : 0) + (tall ? 2 : 1); }
+
+void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4)
 {
     const int groups = (int)(K / kGroup);
     const int n_tiles = (int)((N + kTileN - 1) / kTileN);
@@ -1191,7 +1270,7 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
         for (int sp = 1; sp <= groups; ++sp) {
             const int gps = (groups + sp - 1) / sp;
             if ((groups + gps - 1) / gps != sp) continue;
-            const Choice c = score(*v, base, groups, sp, av, K, N);
+            const Choice c = score(*v, base, groups, sp, av, K, N, bits);
             if (c.us < best.us * 0.98) best = c;
         }
     }
@@ -1217,7 +1296,7 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     const int gps = (groups + best.splits - 1) / best.splits;
     const int splits = (groups + gps - 1) / gps;
     const int64_t split_tiles = splits > 1 ? base - full : 0;
-    pl->kernel = best.v == &kTall ? 2 : 1;
+    pl->kernel = small_kernel_id(best.v == &kTall, bits);
     pl->tile_m = kTileM;
     pl->tile_n = kTileN;
     pl->m_blocks = m_blocks;
@@ -1242,10 +1321,130 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 size_t plan_lds_bytes(int64_t M, const w4_plan &pl)
 {
     const int rows = M < kTileM ? (int)M : kTileM;
-    const Variant &v = pl.kernel == 2 ? kTall : kWide;
+    const Variant &v = (pl.kernel == 2 || pl.kernel == 5) ? kTall : kWide;
     const size_t tiles = (size_t)v.waves * kPipeWaveBytes;
     const size_t red = (size_t)v.waves * rows * kTileN * 4;
     return tiles > red ? tiles : red;
+}
+
+// Small-M launches: one instantiation per (vectorized loads, waves, activation chunks per
+// lane, code width); every shape keeps 3 waves per SIMD.
+template <int BITS, int WAVES>
+void launch_small(int av, bool vec, dim3 grid, size_t lds, hipStream_t s, const SmallParams &p)
+{
+#define W4_LAUNCH(V, AVV) \
+    hipLaunchKernelGGL((w4a16_kernel<V, WAVES, AVV, kOccupancy, BITS>), grid, dim3(WAVES * kWave), lds, s, p)
+#define W4_LAUNCH_AV(V) \
+    switch (av) { case 1: W4_LAUNCH(V, 1); break; case 2: W4_LAUNCH(V, 2); break; \
+                  case 3: W4_LAUNCH(V, 3); break; default: W4_LAUNCH(V, 4); break; }
+    if (vec) { W4_LAUNCH_AV(true) } else { W4_LAUNCH_AV(false) }
+#undef W4_LAUNCH_AV
+#undef W4_LAUNCH
+}
+
+// The GEMM for either code width: host validation, plan, workspace, launches.
+w4_status run_gemm(int bits, const char *name, const void *A_bf16, const uint32_t *Wq, const void *scales_f16,
+                   const uint8_t *zeros, float *C, int64_t M, int64_t K, int64_t N, void *stream)
+{
+    if (!A_bf16 || !Wq || !scales_f16 || !zeros || !C) {
+        set_error("%s: a required pointer is NULL", name);
+        return W4_ERR_NULL;
+    }
+    w4_status st = validate_gemm_shape(M, K, N, bits);
+    if (st != W4_OK) return st;
+    if (!aligned(A_bf16, 16) || !aligned(Wq, 16) || !aligned(C, 16) || !aligned(scales_f16, 2)) {
+        set_error("%s: A, Wq and C must be 16-byte aligned and scales 2-byte aligned", name);
+        return W4_ERR_ALIGN;
+    }
+    int dev = -1;
+    st = check_device(&dev);
+    if (st != W4_OK) return st;
+
+    w4_plan pl;
+    if (bits == 8)
+        make_small_plan(M, K, N, &pl, 8);
+    else
+        make_plan(M, K, N, &pl);
+    hipStream_t s = (hipStream_t)stream;
+    unsigned *count = nullptr;
+    float *part = nullptr;
+    if (pl.workspace_bytes > 0) {
+        // small-M: [tile counters][partial tiles]; large-M: [split slices] only
+        const int64_t tiles = pl.kernel == 3 ? 0 : (int64_t)pl.n_tiles * pl.m_blocks - pl.full_tiles;
+        st = get_workspace(dev, s, (size_t)tiles, (size_t)(pl.workspace_bytes - tiles * 4), &count, &part);
+        if (st != W4_OK) return st;
+    }
+    const dim3 grid((unsigned)pl.workgroups);
+    if (pl.kernel == 3) {
+        LargeParams q;
+        q.A = (const uint16_t *)A_bf16;
+        q.Wq = Wq;
+        q.S = (const uint16_t *)scales_f16;
+        q.Z = zeros;
+        q.C = C;
+        q.part = part;
+        q.stride = (M * N + 3) / 4 * 4;
+        q.M = M;
+        q.K = K;
+        q.N = N;
+        q.groups = (int)(K / kGroup);
+        q.splits = pl.splits;
+        q.gps = pl.groups_per_split;
+        q.n_tiles = pl.n_tiles;
+        q.m_blocks = pl.m_blocks;
+        q.block_rows = pl.tile_m;
+#define W4_LAUNCH_L(RTV) hipLaunchKernelGGL((w4a16_mfma_kernel<RTV>), grid, dim3(kLThreads), 0, s, q)
+        switch ((pl.tile_m + 31) / 32) {
+        case 1: W4_LAUNCH_L(1); break;
+        case 2: W4_LAUNCH_L(2); break;
+        case 3: W4_LAUNCH_L(3); break;
+        case 4: W4_LAUNCH_L(4); break;
+        default: W4_LAUNCH_L(5); break;
+        }
+#undef W4_LAUNCH_L
+        if (pl.splits > 1) {
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return hip_fail(name, e);
+            const int64_t n4 = M * N / 4;
+            int64_t blocks = (n4 + 255) / 256;
+            blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+            hipLaunchKernelGGL(w4a16_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, C, M * N, q.stride,
+                               pl.splits);
+        }
+    } else {
+        SmallParams p;
+        p.A = (const uint16_t *)A_bf16;
+        p.Wq = Wq;
+        p.S = (const uint16_t *)scales_f16;
+        p.Z = zeros;
+        p.C = C;
+        p.part = part;
+        p.count = count;
+        p.M = M;
+        p.K = K;
+        p.N = N;
+        p.groups = (int)(K / kGroup);
+        p.splits = pl.splits;
+        p.gps = pl.groups_per_split;
+        p.n_tiles = pl.n_tiles;
+        p.m_blocks = pl.m_blocks;
+        p.full_tiles = pl.full_tiles;
+        const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros, 4);
+        const size_t lds = plan_lds_bytes(M, pl);
+        const int rows = M < kTileM ? (int)M : kTileM;
+        const int av = (rows + 3) / 4;
+        const bool tall = pl.kernel == 2 || pl.kernel == 5;
+        if (bits == 8) {
+            if (tall) launch_small<8, kTall.waves>(av, vec, grid, lds, s, p);
+            else launch_small<8, kWide.waves>(av, vec, grid, lds, s, p);
+        } else {
+            if (tall) launch_small<4, kTall.waves>(av, vec, grid, lds, s, p);
+            else launch_small<4, kWide.waves>(av, vec, grid, lds, s, p);
+        }
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(name, e);
+    return W4_OK;
 }
 
 }  // namespace
@@ -1284,104 +1483,25 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
                      const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N,
                      void *stream)
 {
-    if (!A_bf16 || !Wq || !scales_f16 || !zeros_u4 || !C) {
-        set_error("w4a16_gemm: a required pointer is NULL");
+    return run_gemm(4, "w4a16_gemm", A_bf16, Wq, scales_f16, zeros_u4, C, M, K, N, stream);
+}
+
+w4_status w8a16_gemm(const void *A_bf16, const uint32_t *Wq8, const void *scales_f16,
+                     const uint8_t *zeros_u8, float *C, int64_t M, int64_t K, int64_t N,
+                     void *stream)
+{
+    return run_gemm(8, "w8a16_gemm", A_bf16, Wq8, scales_f16, zeros_u8, C, M, K, N, stream);
+}
+
+w4_status w8a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out)
+{
+    if (!out) {
+        set_error("w8a16_plan: out is NULL");
         return W4_ERR_NULL;
     }
-    w4_status st = validate_gemm_shape(M, K, N);
+    w4_status st = validate_gemm_shape(M, K, N, 8);
     if (st != W4_OK) return st;
-    if (!aligned(A_bf16, 16) || !aligned(Wq, 16) || !aligned(C, 16) || !aligned(scales_f16, 2)) {
-        set_error("w4a16_gemm: A, Wq and C must be 16-byte aligned and scales 2-byte aligned");
-        return W4_ERR_ALIGN;
-    }
-    int dev = -1;
-    st = check_device(&dev);
-    if (st != W4_OK) return st;
-
-    w4_plan pl;
-    make_plan(M, K, N, &pl);
-    hipStream_t s = (hipStream_t)stream;
-    unsigned *count = nullptr;
-    float *part = nullptr;
-    if (pl.workspace_bytes > 0) {
-        // small-M: [tile counters][partial tiles]; large-M: [split slices] only
-        const int64_t tiles = pl.kernel == 3 ? 0 : (int64_t)pl.n_tiles * pl.m_blocks - pl.full_tiles;
-        st = get_workspace(dev, s, (size_t)tiles, (size_t)(pl.workspace_bytes - tiles * 4), &count, &part);
-        if (st != W4_OK) return st;
-    }
-    const dim3 grid((unsigned)pl.workgroups);
-    if (pl.kernel == 3) {
-        LargeParams q;
-        q.A = (const uint16_t *)A_bf16;
-        q.Wq = Wq;
-        q.S = (const uint16_t *)scales_f16;
-        q.Z = zeros_u4;
-        q.C = C;
-        q.part = part;
-        q.stride = (M * N + 3) / 4 * 4;
-        q.M = M;
-        q.K = K;
-        q.N = N;
-        q.groups = (int)(K / kGroup);
-        q.splits = pl.splits;
-        q.gps = pl.groups_per_split;
-        q.n_tiles = pl.n_tiles;
-        q.m_blocks = pl.m_blocks;
-        q.block_rows = pl.tile_m;
-#define W4_LAUNCH_L(RTV) hipLaunchKernelGGL((w4a16_mfma_kernel<RTV>), grid, dim3(kLThreads), 0, s, q)
-        switch ((pl.tile_m + 31) / 32) {
-        case 1: W4_LAUNCH_L(1); break;
-        case 2: W4_LAUNCH_L(2); break;
-        case 3: W4_LAUNCH_L(3); break;
-        case 4: W4_LAUNCH_L(4); break;
-        default: W4_LAUNCH_L(5); break;
-        }
-#undef W4_LAUNCH_L
-        if (pl.splits > 1) {
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return hip_fail("w4a16_gemm launch", e);
-            const int64_t n4 = M * N / 4;
-            int64_t blocks = (n4 + 255) / 256;
-            blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
-            hipLaunchKernelGGL(w4a16_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, C, M * N, q.stride,
-                               pl.splits);
-        }
-    } else {
-        SmallParams p;
-        p.A = (const uint16_t *)A_bf16;
-        p.Wq = Wq;
-        p.S = (const uint16_t *)scales_f16;
-        p.Z = zeros_u4;
-        p.C = C;
-        p.part = part;
-        p.count = count;
-        p.M = M;
-        p.K = K;
-        p.N = N;
-        p.groups = (int)(K / kGroup);
-        p.splits = pl.splits;
-        p.gps = pl.groups_per_split;
-        p.n_tiles = pl.n_tiles;
-        p.m_blocks = pl.m_blocks;
-        p.full_tiles = pl.full_tiles;
-        const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros_u4, 4);
-        const size_t lds = plan_lds_bytes(M, pl);
-        const int rows = M < kTileM ? (int)M : kTileM;
-        const int av = (rows + 3) / 4;
-#define W4_LAUNCH(V, WV, AVV, OCCV) hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, OCCV>), grid, dim3(WV * kWave), lds, s, p)
-#define W4_LAUNCH_AV(V, WV, OCCV) \
-    switch (av) { case 1: W4_LAUNCH(V, WV, 1, OCCV); break; case 2: W4_LAUNCH(V, WV, 2, OCCV); break; \
-                  case 3: W4_LAUNCH(V, WV, 3, OCCV); break; default: W4_LAUNCH(V, WV, 4, OCCV); break; }
-        if (pl.kernel == 2) {
-            if (vec) { W4_LAUNCH_AV(true, 12, kOccupancy) } else { W4_LAUNCH_AV(false, 12, kOccupancy) }
-        } else {
-            if (vec) { W4_LAUNCH_AV(true, 4, kOccupancy) } else { W4_LAUNCH_AV(false, 4, kOccupancy) }
-        }
-#undef W4_LAUNCH_AV
-#undef W4_LAUNCH
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail("w4a16_gemm launch", e);
+    make_small_plan(M, K, N, out, 8);
     return W4_OK;
 }
 
@@ -1466,6 +1586,33 @@ w4_status w4_pack(const uint8_t *q_u4, uint32_t *Wq, int64_t K, int64_t N, void 
                        q_u4, Wq, K / 8, N);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail("w4_pack launch", e);
+    return W4_OK;
+}
+
+w4_status w8_pack(const uint8_t *q_u8, uint32_t *Wq8, int64_t K, int64_t N, void *stream)
+{
+    if (!q_u8 || !Wq8) {
+        set_error("w8_pack: a required pointer is NULL");
+        return W4_ERR_NULL;
+    }
+    if (K < 4 || K % 4 != 0 || N < 1 || K > ((int64_t)1 << 40) / N) {
+        set_error("w8_pack: shape K=%lld N=%lld: need K>=4, K%%4==0, N>=1", (long long)K, (long long)N);
+        return W4_ERR_SHAPE;
+    }
+    if (!aligned(Wq8, 4)) {
+        set_error("w8_pack: Wq8 must be 4-byte aligned");
+        return W4_ERR_ALIGN;
+    }
+    int dev = -1;
+    w4_status st = check_device(&dev);
+    if (st != W4_OK) return st;
+    const int64_t total = (K / 4) * N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(w8_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       q_u8, Wq8, K / 4, N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("w8_pack launch", e);
     return W4_OK;
 }
 

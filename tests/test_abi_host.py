@@ -13,7 +13,8 @@ import int4_weight_only_gemm_amd as w4
 
 def test_library_exports_every_declared_symbol():
     names = w4.header_functions()
-    assert set(names) >= {"w4a16_gemm", "w4_pack", "w4a16_plan", "w4_status_string", "w4_last_error"}
+    assert set(names) >= {"w4a16_gemm", "w4_pack", "w4a16_plan", "w4_status_string", "w4_last_error",
+                          "w8a16_gemm", "w8_pack", "w8a16_plan", "w4_quantize", "w4_read_probe"}
     lib = w4.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/w4a16.h but not exported"
@@ -33,25 +34,50 @@ def _gemm(*args):
     return w4.lib().w4a16_gemm(*args)
 
 
+GEMMS = {"w4a16": lambda *a: w4.lib().w4a16_gemm(*a), "w8a16": lambda *a: w4.lib().w8a16_gemm(*a)}
+
+
+@pytest.mark.parametrize("which", sorted(GEMMS))
 @pytest.mark.parametrize("ptrs", [
     (None, W16, S8, Z4, C16), (A16, None, S8, Z4, C16), (A16, W16, None, Z4, C16),
     (A16, W16, S8, None, C16), (A16, W16, S8, Z4, None)])
-def test_null_pointers(ptrs):
-    assert _gemm(*ptrs, 5, 128, 64, None) == 1
+def test_null_pointers(ptrs, which):
+    assert GEMMS[which](*ptrs, 5, 128, 64, None) == 1
     assert w4.lib().w4_last_error()
 
 
+@pytest.mark.parametrize("which", sorted(GEMMS))
 @pytest.mark.parametrize("mkn", [(0, 128, 64), (5, 0, 64), (5, 64, 64), (5, 129, 64), (5, 200, 64),
                                  (5, 128, 0), (-1, 128, 8), (5, -128, 8), (1 << 31, 1 << 20, 1 << 20)])
-def test_bad_shapes(mkn):
-    assert _gemm(A16, W16, S8, Z4, C16, *mkn, None) == 2
+def test_bad_shapes(mkn, which):
+    assert GEMMS[which](A16, W16, S8, Z4, C16, *mkn, None) == 2
 
 
+def test_packed_weight_limit_follows_code_width():
+    # packed codes must stay below 2 GiB: K*N/2 bytes for 4-bit codes, K*N bytes for 8-bit
+    K, N = 1 << 16, 1 << 15          # 2^31 weights: 1 GiB packed at 4 bits, 2 GiB at 8 bits
+    assert w4.plan(1, K, N)["splits"] >= 1
+    with pytest.raises(w4.W4Error):
+        w4.plan(1, K, N, bits=8)
+    assert w4.plan(1, K, N // 2, bits=8)["splits"] >= 1
+
+
+@pytest.mark.parametrize("which", sorted(GEMMS))
 @pytest.mark.parametrize("ptrs", [
     (A16 + 2, W16, S8, Z4, C16), (A16, W16 + 4, S8, Z4, C16), (A16, W16, S8, Z4, C16 + 8),
     (A16, W16, S8 + 1, Z4, C16)])
-def test_misaligned(ptrs):
-    assert _gemm(*ptrs, 5, 128, 64, None) == 3
+def test_misaligned(ptrs, which):
+    assert GEMMS[which](*ptrs, 5, 128, 64, None) == 3
+
+
+def test_pack8_validation():
+    lib = w4.lib()
+    assert lib.w8_pack(None, W16, 4, 4, None) == 1
+    assert lib.w8_pack(A16, None, 4, 4, None) == 1
+    assert lib.w8_pack(A16, W16, 6, 4, None) == 2
+    assert lib.w8_pack(A16, W16, 0, 4, None) == 2
+    assert lib.w8_pack(A16, W16, 4, 0, None) == 2
+    assert lib.w8_pack(A16, W16 + 2, 4, 4, None) == 3
 
 
 def test_pack_validation():
@@ -112,31 +138,36 @@ def test_plan_covers_shapes():
     # a balanced wide plan runs whole rounds of 256 tiles unsplit and splits the rest
     import synth
     seen = set()
-    for wl in synth.WORKLOADS.values():
-        for g in wl.gemms:
-            key = (g.M, g.K, g.N)
-            if key in seen:
-                continue
-            seen.add(key)
-            p = w4.plan(*key)
-            groups = g.K // 128
-            assert (p["kernel"] == 3) == (g.M >= 64 or (g.M >= 17 and g.K * g.N >= 1 << 25))
+    shapes = [(g.M, g.K, g.N, g.bits) for wl in synth.WORKLOADS.values() for g in wl.gemms]
+    shapes += [(M, K, N, 8) for M in (1, 5, 16, 17, 40, 64, 160) for K, N in ((3584, 4608), (18944, 3584), (128, 3))]
+    for key in shapes:
+        if key in seen:
+            continue
+        seen.add(key)
+        M, K, N, bits = key
+        p = w4.plan(M, K, N, bits=bits)
+        groups = K // 128
+        if bits == 8:  # every row count runs on the 8-bit small-M kernel
+            assert p["kernel"] in (4, 5)
+        else:
+            assert (p["kernel"] == 3) == (M >= 64 or (M >= 17 and K * N >= 1 << 25))
+        if True:
             if p["kernel"] == 3:
                 assert p["tile_n"] == 256 and p["tile_m"] <= 160
             else:
                 assert (p["tile_m"], p["tile_n"]) == (16, 64)
-            assert p["n_tiles"] * p["tile_n"] >= g.N > (p["n_tiles"] - 1) * p["tile_n"]
-            assert p["m_blocks"] * p["tile_m"] >= g.M > (p["m_blocks"] - 1) * p["tile_m"]
+            assert p["n_tiles"] * p["tile_n"] >= N > (p["n_tiles"] - 1) * p["tile_n"]
+            assert p["m_blocks"] * p["tile_m"] >= M > (p["m_blocks"] - 1) * p["tile_m"]
             assert p["splits"] * p["groups_per_split"] >= groups
             assert (p["splits"] - 1) * p["groups_per_split"] < groups
             tiles = p["n_tiles"] * p["m_blocks"]
             full = p["full_tiles"]
             assert full % 256 == 0 and 0 <= full < tiles
-            assert full == 0 or (p["kernel"] == 1 and p["splits"] > 1)
+            assert full == 0 or (p["kernel"] in (1, 4) and p["splits"] > 1)
             assert p["workgroups"] == full + (tiles - full) * p["splits"]
             assert (p["workspace_bytes"] > 0) == (p["splits"] > 1)
-            if p["kernel"] in (1, 2):  # every workgroup resident at once
-                assert p["workgroups"] <= 256 * (3 if p["kernel"] == 1 else 1) or p["splits"] == 1
+            if p["kernel"] in (1, 2, 4, 5):  # every workgroup resident at once
+                assert p["workgroups"] <= 256 * (3 if p["kernel"] in (1, 4) else 1) or p["splits"] == 1
     with pytest.raises(w4.W4Error):
         w4.plan(5, 100, 64)
 
