@@ -75,6 +75,10 @@ class Oracle:
         lib.oracle_w8_pack.restype = ctypes.c_int
         lib.oracle_w8_unpack.argtypes = [vp, vp, i64, i64]
         lib.oracle_w8_unpack.restype = ctypes.c_int
+        lib.oracle_a4_quantize.argtypes = [vp, vp, vp, i64, i64]
+        lib.oracle_a4_quantize.restype = ctypes.c_int
+        lib.oracle_w4a4_gemm.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp, vp, ctypes.c_int]
+        lib.oracle_w4a4_gemm.restype = ctypes.c_int
         self._lib = lib
 
     # -- decoders -----------------------------------------------------------------
@@ -148,6 +152,49 @@ class Oracle:
         if rc:
             raise ValueError(f"oracle unpack8 rejected shape {Wq8.shape}")
         return out
+
+    # -- 4-bit activations (W4A4) --------------------------------------------------
+    def quantize_activations(self, A: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+        """Symmetric 4-bit activations per row and group of 128 (see the C source).
+
+        A: uint16 bfloat16 bits [M, K].  Returns (Aq uint32 [M, K/8] offset-binary nibbles,
+        As float32 [M, K/128] scales).
+        """
+        A = np.ascontiguousarray(A, dtype=np.uint16)
+        M, K = A.shape
+        Aq = np.empty((M, K // 8), dtype=np.uint32)
+        As = np.empty((M, K // 128), dtype=np.float32)
+        rc = self._lib.oracle_a4_quantize(_ptr(A), _ptr(Aq), _ptr(As), M, K)
+        if rc:
+            raise ValueError(f"oracle a4 quantize rejected shape {A.shape}")
+        return Aq, As
+
+    def gemm_a4(self, Aq: np.ndarray, As: np.ndarray, Wq: np.ndarray, S: np.ndarray, Z: np.ndarray,
+                cols: Optional[np.ndarray] = None, threads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """W4A4: (C, Cabs) float64 [M, ncols] from 4-bit activations (Aq, As) and the 4-bit
+        weight format (Wq [K/8, N], S, Z)."""
+        Aq = np.ascontiguousarray(Aq, dtype=np.uint32)
+        As = np.ascontiguousarray(As, dtype=np.float32)
+        Wq = np.ascontiguousarray(Wq, dtype=np.uint32)
+        S = np.ascontiguousarray(S, dtype=np.uint16)
+        Z = np.ascontiguousarray(Z, dtype=np.uint8)
+        M, KB = Aq.shape
+        K = KB * 8
+        N = Wq.shape[1]
+        if Wq.shape[0] * 8 != K or As.shape != (M, K // 128) or S.shape != (K // 128, N) or Z.shape != (K // 128, N):
+            raise ValueError("inconsistent shapes")
+        if cols is not None:
+            cols = np.ascontiguousarray(cols, dtype=np.int64)
+            nc = cols.size
+        else:
+            nc = N
+        C = np.empty((M, nc), dtype=np.float64)
+        Cabs = np.empty((M, nc), dtype=np.float64)
+        rc = self._lib.oracle_w4a4_gemm(_ptr(Aq), _ptr(As), _ptr(Wq), _ptr(S), _ptr(Z), M, K, N, _ptr(cols), nc,
+                                        _ptr(C), _ptr(Cabs), int(threads))
+        if rc:
+            raise ValueError(f"oracle rejected the shape M={M} K={K} N={N} (rc={rc})")
+        return C, Cabs
 
     # -- the GEMM -----------------------------------------------------------------
     def gemm(self, A: np.ndarray, Wq: np.ndarray, S: np.ndarray, Z: np.ndarray,

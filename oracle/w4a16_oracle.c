@@ -2,8 +2,8 @@
  * w4a16_oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
  * The plain, slow, obviously correct CPU reference for the group-wise INT4
- * weight-only GEMM (W4A16), its 8-bit variant (W8A16, further down) and the 4-bit
- * quantizer.  Only the tests, the smoke check and the bench's CPU
+ * weight-only GEMM (W4A16), its 8-bit variant (W8A16, further down), the 4-bit
+ * activation variant (W4A4) with its activation quantizer, and the 4-bit weight quantizer.  Only the tests, the smoke check and the bench's CPU
  * baseline leg load it; the product path never does.  It shares no source, header,
  * table or helper with the HIP library.
  *
@@ -281,6 +281,85 @@ int oracle_w8_unpack(const uint32_t *Wq8, uint8_t *q, int64_t K, int64_t N)
     if (K < 4 || K % 4 != 0 || N < 1) return -1;
     for (int64_t k = 0; k < K; ++k)
         for (int64_t n = 0; n < N; ++n) q[k * N + n] = (uint8_t)oracle_byte_code(Wq8, N, k, n);
+    return 0;
+}
+
+/*
+ * The 4-bit-activation variant (W4A4).  "When Do Quantized Drafts Help Speculative
+ * Decoding?", "What is open": QSPEC drafts with W4A4 and verifies with W4A16 on the same
+ * 4-bit weights, and the unified W4A4 kernel was the missing piece.  The pages print no
+ * activation format; the plainest reading keeps the weights in the W4A16 storage format
+ * above and quantizes activations symmetrically to 4 bits per row and group of 128 along K:
+ *
+ *   amax     = max_{k in g} |A[m,k]|                       (binary32; exact from bfloat16)
+ *   sa[m,g]  = amax / 7                                    (binary32, IEEE division)
+ *   qa[m,k]  = clamp(rint(A[m,k] / sa[m,g]), -8, 7)        (rint ties to even; 0 if sa == 0)
+ *   Aq       uint32 [M, K/8]; nibble j of Aq[m,kb] is qa[m, 8kb+j] + 8 (offset binary)
+ *
+ *   C[m,n]   = sum_g sa[m,g] * s[g,n] * sum_{k in g} qa[m,k] * (q[k,n] - z[g,n])
+ *
+ * Every term sa * s * qa * (q - z) is exact in binary64 (24 + 11 + 4 + 5 significant
+ * bits); the sums run in plain k order, and Cabs sums their magnitudes.
+ */
+int oracle_a4_quantize(const uint16_t *A, uint32_t *Aq, float *As, int64_t M, int64_t K)
+{
+    if (M < 1 || K < ORACLE_GROUP || K % ORACLE_GROUP != 0) return -1;
+    memset(Aq, 0, (size_t)M * (size_t)(K / 8) * sizeof(uint32_t));
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t g = 0; g < K / ORACLE_GROUP; ++g) {
+            float amax = 0.0f;
+            for (int64_t k = g * ORACLE_GROUP; k < (g + 1) * ORACLE_GROUP; ++k)
+                amax = fmaxf(amax, fabsf((float)oracle_bf16_to_f64(A[m * K + k])));
+            const float sa = amax / 7.0f;
+            As[m * (K / ORACLE_GROUP) + g] = sa;
+            for (int64_t k = g * ORACLE_GROUP; k < (g + 1) * ORACLE_GROUP; ++k) {
+                const float a = (float)oracle_bf16_to_f64(A[m * K + k]);
+                const int qa = sa == 0.0f ? 0 : (int)fminf(fmaxf(rintf(a / sa), -8.0f), 7.0f);
+                Aq[m * (K / 8) + k / 8] |= (uint32_t)(qa + 8) << (4 * (k % 8));
+            }
+        }
+    return 0;
+}
+
+/* The signed 4-bit activation code of row m, column k. */
+static inline int oracle_act_code(const uint32_t *Aq, int64_t K, int64_t m, int64_t k)
+{
+    return (int)((Aq[m * (K / 8) + k / 8] >> (4 * (k % 8))) & 0xFu) - 8;
+}
+
+int oracle_w4a4_gemm(const uint32_t *Aq, const float *As, const uint32_t *Wq, const uint16_t *S,
+                     const uint8_t *Z, int64_t M, int64_t K, int64_t N,
+                     const int64_t *cols, int64_t ncols, double *C, double *Cabs, int nthreads)
+{
+    if (M < 1 || N < 1 || K < ORACLE_GROUP || K % ORACLE_GROUP != 0) return -1;
+    if (!cols) ncols = N;
+    if (ncols < 1) return -1;
+    for (int64_t c = 0; cols && c < ncols; ++c)
+        if (cols[c] < 0 || cols[c] >= N) return -1;
+    const int64_t G = K / ORACLE_GROUP;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < ncols; ++c) {
+        const int64_t n = cols ? cols[c] : c;
+        for (int64_t m = 0; m < M; ++m) {
+            double total = 0.0, magnitude = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t gk = k / ORACLE_GROUP;
+                const double wdq = (double)(oracle_code(Wq, N, k, n) - (Z[gk * N + n] & 0xF)) *
+                                   oracle_f16_to_f64(S[gk * N + n]);             /* exact: 5 x 11 bits */
+                const double adq = (double)oracle_act_code(Aq, K, m, k) * (double)As[m * G + gk];  /* 4 x 24 */
+                const double term = adq * wdq;                                      /* exact: 27 x 16 bits */
+                total += term;
+                magnitude += fabs(term);
+            }
+            C[m * ncols + c] = total;
+            if (Cabs) Cabs[m * ncols + c] = magnitude;
+        }
+    }
     return 0;
 }
 

@@ -26,6 +26,10 @@ Value recipe (the pages give no distribution; these are the stated synthetic inp
 "Current pilot setup"): q and z uniform 0..255 (words: 4 i.i.d. uniform bytes), and the
 4-bit scale recipe divided by 16, s = (|N(0, 1)| * 0.02 + 1e-3) / 16, so that the dequantized
 weights span the same range as the 4-bit ones.
+4-bit activations (the W4A4 draft of "When Do Quantized Drafts Help Speculative Decoding?",
+"What is open"): codes uniform -8..7 as offset-binary nibbles (uniform u32 words), one
+float32 scale per row and group of 128, (2.5 + 0.3 |N(0, 1)|) / 7, about what the largest
+of 128 standard normal values gives.  The weights are the 4-bit recipe above.
 Every (layer, projection) gets its own PCG64 stream spawned from
 SeedSequence([0, workload_id, layer, projection_index]) so any single GEMM can be
 regenerated without drawing the others.
@@ -73,6 +77,7 @@ class GemmSpec:
     seed: Tuple[int, ...]  # SeedSequence entropy for this GEMM's draws
     q_as_bytes: bool = False  # draw unpacked u8 codes (packed later by the pack entry point)
     bits: int = 4             # code width: 4 (W4A16) or 8 (W8A16)
+    act4: bool = False        # 4-bit activations (W4A4) instead of bfloat16
 
     @property
     def weight_bytes(self) -> int:
@@ -101,12 +106,12 @@ class Workload:
         return sum(g.flops for g in self.gemms)
 
 
-def _model_pass(wid: int, model: str, M: int, layers: int, bits: int = 4) -> Tuple[GemmSpec, ...]:
+def _model_pass(wid: int, model: str, M: int, layers: int, bits: int = 4, act4: bool = False) -> Tuple[GemmSpec, ...]:
     out = []
     for layer in range(layers):
         for pi, proj in enumerate(PROJ_ORDER):
             K, N = MODEL_SHAPES[model][proj]
-            out.append(GemmSpec(f"L{layer}.{proj}", M, K, N, (0, wid, layer, pi), bits=bits))
+            out.append(GemmSpec(f"L{layer}.{proj}", M, K, N, (0, wid, layer, pi), bits=bits, act4=act4))
     return tuple(out)
 
 
@@ -163,6 +168,12 @@ WORKLOADS: Dict[str, Workload] = {
             _model_pass(7, "qwen2.5-7b", 80, 28),
         ),
         Workload(
+            "llama2-7b-w4a4-draft-m32",
+            "W4A4 draft step of a Llama-2-7B-shaped model at batch 32 (one token per sequence, M=32), "
+            "32 layers x {qkv,o,gate_up,down}, 4-bit activations on the 4-bit weights",
+            _model_pass(9, "llama2-7b", 32, 32, act4=True),
+        ),
+        Workload(
             "llama2-7b-batched-verify-m160",
             "batched verify of a Llama-2-7B-shaped target, M=32x5=160, 32 layers x {qkv,o,gate_up,down}",
             _model_pass(5, "llama2-7b", 160, 32),
@@ -200,6 +211,8 @@ class GemmInputs:
     q: Optional[np.ndarray]  # uint8 [K, N] unpacked codes, when drawn as bytes
     S: np.ndarray      # uint16 [K/128, N] float16 bit patterns
     Z: np.ndarray      # uint8 [K/128, N]  zero points (4-bit: low nibble used)
+    Aq: Optional[np.ndarray] = None  # uint32 [M, K/8] 4-bit activation codes (W4A4), else None
+    As: Optional[np.ndarray] = None  # float32 [M, K/128] activation scales (W4A4), else None
 
 
 def _rng(seed: Tuple[int, ...]) -> np.random.Generator:
@@ -250,14 +263,24 @@ def generate(spec: GemmSpec) -> GemmInputs:
     Z = draw_zeros(wr, G, N, spec.bits)
     ar = _rng(tuple(spec.seed) + (0,))
     A = draw_activations(ar, M, K)
+    if spec.act4:
+        Aq, As = draw_act4(ar, M, K)
+        return GemmInputs(A=A, Wq=Wq, q=q, S=S, Z=Z, Aq=Aq, As=As)
     return GemmInputs(A=A, Wq=Wq, q=q, S=S, Z=Z)
 
 
+def draw_act4(rng: np.random.Generator, M: int, K: int) -> Tuple[np.ndarray, np.ndarray]:
+    """4-bit activation codes (offset-binary nibbles in uniform u32 words) and float32 scales."""
+    Aq = rng.integers(0, 1 << 32, size=(M, K // 8), dtype=np.uint32)
+    As = ((2.5 + 0.3 * np.abs(rng.standard_normal((M, K // GROUP)))) / 7.0).astype(np.float32)
+    return Aq, As
+
+
 def generate_custom(M: int, K: int, N: int, seed: int, q_as_bytes: bool = False,
-                    z_range: Optional[Tuple[int, int]] = None, bits: int = 4) -> GemmInputs:
+                    z_range: Optional[Tuple[int, int]] = None, bits: int = 4, act4: bool = False) -> GemmInputs:
     """Inputs for an arbitrary shape (parity grids, edge cases) with the standard recipe."""
     spec = GemmSpec("custom", M, K, N, (0, 99 + (bits == 8), seed, M * 1_000_003 + K * 1009 + N), q_as_bytes,
-                    bits=bits)
+                    bits=bits, act4=act4)
     x = generate(spec)
     if z_range is not None and z_range != (0, 1 << bits):
         r = _rng((0, 98, seed))

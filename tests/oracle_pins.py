@@ -26,7 +26,13 @@ What pins what:
     (tests/golden/closed_forms8.txt), round trips against numpy's byte view of the words,
     the identity and all-ones cases with zero points up to 254, one-hot rows, exact zeros,
     exact rational brute force, a BLAS float64 matmul of the dequantized W, column sampling,
-    thread count and scale invariance.
+    thread count and scale invariance;
+  * 4-bit activations: hand-worked words (tests/golden/act4_words.txt), exact codes and
+    scales on the grid, ties to even, all-zero groups, numpy's binary32 division for the
+    scale with the half-step error bound, power-of-two scaling and negation; the W4A4
+    product by hand-computed closed forms (tests/golden/closed_forms_a4.txt), rational brute
+    force, a BLAS matmul, one-hot rows, exact zeros, the identity case, and equality with
+    the W4A16 product where the dequantized activations are exact bfloat16 values.
 """
 from __future__ import annotations
 
@@ -652,6 +658,234 @@ def pin_w8_sampling_scaling_threads(o):
     assert np.array_equal(C3, 2.0 * C)
 
 
+# ---------------------------------------------------------------------------------------
+# 4-bit activations (W4A4): symmetric codes per row and group of 128, offset-binary nibbles.
+def np_act_codes(Aq):
+    """Signed activation codes [M, K] from the packed words (numpy decoding)."""
+    Aq = np.asarray(Aq, np.uint32)
+    M, KB = Aq.shape
+    shifts = (4 * np.arange(8, dtype=np.uint32))[None, None, :]
+    return (((Aq[:, :, None] >> shifts) & 0xF).reshape(M, KB * 8).astype(np.int64) - 8)
+
+
+def np_pack_act(qa):
+    """Pack signed codes [M, K] (-8..7) into offset-binary words [M, K/8]."""
+    u = (np.asarray(qa, np.int64) + 8).astype(np.uint32)
+    M, K = u.shape
+    u = u.reshape(M, K // 8, 8)
+    w = np.zeros((M, K // 8), np.uint32)
+    for j in range(8):
+        w |= u[:, :, j] << np.uint32(4 * j)
+    return w
+
+
+def pin_a4_golden_words(o):
+    rows = []
+    with open(os.path.join(GOLDEN, "act4_words.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                parts = line.split()
+                rows.append(([float(v) for v in parts[:8]], int(parts[8], 16)))
+    assert len(rows) >= 5
+    A = np.zeros((len(rows), 128), np.float32)
+    for i, (vals, _) in enumerate(rows):
+        A[i, 40:48] = vals  # the word of k = 40..47; the rest of the group is 0
+    Aq, As = o.quantize_activations(bf16_bits(A))
+    for i, (_, word) in enumerate(rows):
+        assert As[i, 0] == 1.0, (i, As[i, 0])
+        assert int(Aq[i, 5]) == word, (i, hex(int(Aq[i, 5])), hex(word))
+        assert all(int(Aq[i, j]) == 0x88888888 for j in range(16) if j != 5)
+
+
+def pin_a4_grid_exact(o):
+    # A = qa * 2^e with some |qa| = 7 in each group: the scale is exactly 2^e, codes exact
+    r = np.random.default_rng(41)
+    M, K = 4, 512
+    e = r.integers(-20, 20, size=(M, K // 128))
+    qa = r.integers(-7, 8, size=(M, K))
+    qa[:, ::128] = 7 * r.choice([-1, 1], size=(M, K // 128))
+    A = (qa * np.exp2(np.repeat(e, 128, axis=1))).astype(np.float32)
+    Aq, As = o.quantize_activations(bf16_bits(A))
+    assert np.array_equal(As, np.exp2(e).astype(np.float32))
+    assert np.array_equal(np_act_codes(Aq), qa)
+
+
+def pin_a4_ties_to_even(o):
+    r = np.random.default_rng(42)
+    halves = r.integers(-6, 7, size=(3, 128)) + 0.5
+    halves[:, 0] = 7.0
+    Aq, As = o.quantize_activations(bf16_bits(halves.astype(np.float32)))
+    expect = np.array([[round(v) for v in row] for row in halves])  # Python rounds ties to even
+    assert np.all(As == 1.0)
+    assert np.array_equal(np_act_codes(Aq), expect)
+
+
+def pin_a4_zero_group(o):
+    A = np.zeros((2, 256), np.float32)
+    A[1, 128:] = 0.25
+    A[0, 200] = -3.0
+    Aq, As = o.quantize_activations(bf16_bits(A))
+    assert As[0, 0] == 0.0 and As[1, 0] == 0.0
+    assert np.all(Aq[:, :16] == 0x88888888)
+    qa = np_act_codes(Aq)
+    assert qa[0, 200] == -7 and np.all(np.delete(qa[0, 128:], 72) == 0)
+    assert np.all(qa[1, 128:] == 7)
+
+
+def pin_a4_error_bound_and_scale(o):
+    # random activations: the scale is the group's largest magnitude over 7 (numpy binary32
+    # division), every code is within half a step of A / scale, the largest element maps
+    # to +-7, and no code leaves -8..7
+    r = np.random.default_rng(43)
+    M, K = 6, 1024
+    A = r.standard_normal((M, K)).astype(np.float32) * np.float32(3.0)
+    A[2] *= np.float32(2.0 ** 30)
+    A[3] *= np.float32(2.0 ** -30)
+    Ab = bf16_bits(np_bf16_to_f64(synth.f32_to_bf16_bits(A)).astype(np.float32))
+    Aq, As = o.quantize_activations(Ab)
+    a = np_bf16_to_f64(Ab).reshape(M, K // 128, 128)
+    amax = np.abs(a).max(axis=2).astype(np.float32)
+    assert np.array_equal(As, amax / np.float32(7.0))
+    qa = np_act_codes(Aq).reshape(M, K // 128, 128)
+    assert qa.min() >= -8 and qa.max() <= 7
+    s = As.astype(np.float64)[:, :, None]
+    assert np.all(np.abs(a - s * qa) <= 0.5 * s * (1 + 2.0 ** -20))
+    assert np.all(np.abs(qa).max(axis=2) == 7)
+
+
+def pin_a4_scaling_and_sign(o):
+    r = np.random.default_rng(44)
+    A = synth.f32_to_bf16_bits(r.standard_normal((3, 384), dtype=np.float32))
+    Aq, As = o.quantize_activations(A)
+    a = np_bf16_to_f64(A)
+    Aq2, As2 = o.quantize_activations(bf16_bits((a * 8.0).astype(np.float32)))
+    assert np.array_equal(Aq2, Aq) and np.array_equal(As2, As * np.float32(8.0))
+    Aq3, As3 = o.quantize_activations(bf16_bits((-a).astype(np.float32)))
+    assert np.array_equal(As3, As) and np.array_equal(np_act_codes(Aq3), -np_act_codes(Aq))
+
+
+def pin_a4_gemm_closed_forms(o):
+    rows = []
+    with open(os.path.join(GOLDEN, "closed_forms_a4.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                parts = [p.strip() for p in line.split("|")]
+                rows.append((int(parts[0]), [tuple(float(v) for v in p.split()) for p in parts[1:-1]],
+                             float(parts[-1])))
+    assert len(rows) >= 4
+    for K, groups, expect in rows:
+        G = K // 128
+        N = 3
+        qa = np.zeros((2, K), np.int64)
+        As = np.zeros((2, G), np.float32)
+        q = np.zeros((K, N), np.uint8)
+        S = np.zeros((G, N), np.float64)
+        Z = np.zeros((G, N), np.uint8)
+        for g, (c, sa, qq, zz, ss) in enumerate(groups):
+            qa[:, g * 128:(g + 1) * 128] = int(c)
+            As[:, g] = sa
+            q[g * 128:(g + 1) * 128, :] = int(qq)
+            Z[g, :] = int(zz)
+            S[g, :] = ss
+        assert np.all(As.astype(np.float64) == [[g[1] for g in groups]] * 2)
+        C, Cabs = o.gemm_a4(np_pack_act(qa), As, np_pack(q), f16_bits(S), Z)
+        assert np.all(C == expect), (K, groups, C, expect)
+        assert np.all(Cabs >= np.abs(C))
+
+
+def _a4_inputs(M, K, N, seed):
+    x = synth.generate_custom(M, K, N, seed=seed)
+    Aq, As = (lambda r: (np_pack_act(r.integers(-8, 8, size=(M, K))),
+                         (np.abs(r.standard_normal((M, K // 128))) * 0.1 + 1e-3).astype(np.float32)))(
+        np.random.default_rng(seed))
+    return Aq, As, x
+
+
+def _exact_gemm_a4(Aq, As, Wq, S, Z):
+    qa = np_act_codes(Aq)
+    q = np_unpack(Wq).astype(np.int64)
+    s = np_f16_to_f64(S)
+    z = (np.asarray(Z) & 0xF).astype(np.int64)
+    M, K = qa.shape
+    N = q.shape[1]
+    C = [[Fraction(0)] * N for _ in range(M)]
+    B = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        for k in range(K):
+            g = k // 128
+            w = Fraction(s[g, n]) * int(q[k, n] - z[g, n])
+            for m in range(M):
+                t = Fraction(float(As[m, g])) * int(qa[m, k]) * w
+                C[m][n] += t
+                B[m][n] += abs(t)
+    return C, B
+
+
+def pin_a4_gemm_brute_force(o):
+    for (M, K, N, seed) in ((1, 128, 3, 51), (3, 256, 5, 52), (2, 128, 4, 53)):
+        Aq, As, x = _a4_inputs(M, K, N, seed)
+        C, Cabs = o.gemm_a4(Aq, As, x.Wq, x.S, x.Z)
+        Ce, Be = _exact_gemm_a4(Aq, As, x.Wq, x.S, x.Z)
+        bound_scale = Fraction(K) * Fraction(2) ** -53
+        for m in range(M):
+            for n in range(N):
+                assert abs(Fraction(C[m, n]) - Ce[m][n]) <= bound_scale * Be[m][n], (M, K, N, m, n)
+                assert abs(Fraction(Cabs[m, n]) - Be[m][n]) <= bound_scale * Be[m][n], (M, K, N, m, n)
+
+
+def pin_a4_gemm_numpy_matmul(o):
+    M, K, N = 5, 1536, 1024
+    Aq, As, x = _a4_inputs(M, K, N, 54)
+    C, Cabs = o.gemm_a4(Aq, As, x.Wq, x.S, x.Z)
+    g = np.arange(K) // 128
+    Ad = np_act_codes(Aq) * As.astype(np.float64)[:, g]
+    W = (np_unpack(x.Wq).astype(np.float64) - (x.Z[g] & 0xF)) * np_f16_to_f64(x.S)[g]
+    assert np.all(np.abs(Ad @ W - C) <= 1e-12 * Cabs)
+    assert np.all(np.abs(np.abs(Ad) @ np.abs(W) - Cabs) <= 1e-12 * Cabs)
+
+
+def pin_a4_gemm_one_hot_zero_identity(o):
+    M, K, N = 4, 384, 21
+    Aq, As, x = _a4_inputs(M, K, N, 55)
+    q = np_unpack(x.Wq)
+    s = np_f16_to_f64(x.S)
+    for (m0, k0, c0) in ((0, 0, 1), (1, 7, -8), (3, 130, 7), (2, 383, -3)):
+        qa = np.zeros((M, K), np.int64)
+        qa[m0, k0] = c0
+        C, _ = o.gemm_a4(np_pack_act(qa), As, x.Wq, x.S, x.Z)
+        g0 = k0 // 128
+        expect = float(As[m0, g0]) * c0 * (q[k0].astype(np.float64) - (x.Z[g0] & 0xF)) * s[g0]
+        assert np.array_equal(C[m0], expect) and np.all(np.delete(C, m0, axis=0) == 0.0)
+    C, Cabs = o.gemm_a4(np_pack_act(np.zeros((M, K), np.int64)), As, x.Wq, x.S, x.Z)
+    assert np.all(C == 0.0) and np.all(Cabs == 0.0)
+    C, _ = o.gemm_a4(Aq, As, np_pack(np.repeat(x.Z & 0xF, 128, axis=0)), x.S, x.Z)
+    assert np.all(C == 0.0)
+    # q = z + 1 and s = 1: every column is the row sum of the dequantized activations
+    Zs = np.random.default_rng(56).integers(0, 15, size=x.Z.shape, dtype=np.uint8)
+    C, _ = o.gemm_a4(Aq, As, np_pack(np.repeat(Zs + 1, 128, axis=0)), f16_bits(np.ones(x.S.shape)), Zs)
+    rows = (np_act_codes(Aq) * As.astype(np.float64)[:, np.arange(K) // 128])
+    for m in range(M):
+        assert np.all(np.abs(C[m] - math.fsum(rows[m])) <= K * 2.0 ** -53 * np.abs(rows[m]).sum())
+
+
+def pin_a4_gemm_matches_w4a16_on_exact_activations(o):
+    # with power-of-two activation scales, sa * qa is an exact bfloat16: the W4A4 product
+    # must equal the W4A16 product of those dequantized activations, bit for bit
+    M, K, N = 3, 512, 40
+    r = np.random.default_rng(57)
+    Aq, _, x = _a4_inputs(M, K, N, 58)
+    As = np.exp2(r.integers(-12, 12, size=(M, K // 128))).astype(np.float32)
+    Ad = (np_act_codes(Aq) * As.astype(np.float64)[:, np.arange(K) // 128]).astype(np.float32)
+    C4, _ = o.gemm_a4(Aq, As, x.Wq, x.S, x.Z)
+    C16, _ = o.gemm(bf16_bits(Ad), x.Wq, x.S, x.Z)
+    assert np.array_equal(C4, C16)
+    cols = np.array([39, 0, 17], np.int64)
+    Cs, _ = o.gemm_a4(Aq, As, x.Wq, x.S, x.Z, cols=cols, threads=1)
+    assert np.array_equal(Cs, C4[:, cols])
+
+
 ALL_PINS = [
     pin_f16_encoder_against_numpy,
     pin_quantize_grid_exact,
@@ -686,4 +920,15 @@ ALL_PINS = [
     pin_brute_force8,
     pin_numpy_matmul8,
     pin_w8_sampling_scaling_threads,
+    pin_a4_golden_words,
+    pin_a4_grid_exact,
+    pin_a4_ties_to_even,
+    pin_a4_zero_group,
+    pin_a4_error_bound_and_scale,
+    pin_a4_scaling_and_sign,
+    pin_a4_gemm_closed_forms,
+    pin_a4_gemm_brute_force,
+    pin_a4_gemm_numpy_matmul,
+    pin_a4_gemm_one_hot_zero_identity,
+    pin_a4_gemm_matches_w4a16_on_exact_activations,
 ]

@@ -64,6 +64,20 @@ MUTANTS = {
     "w8_pack_shift_reversed": ("<< (8 * j);", "<< (8 * (3 - j));"),
     "w8_pack_nibbles": ("word |= (uint32_t)q[(4 * kb + j) * N + n] << (8 * j);",
                         "word |= (uint32_t)(q[(4 * kb + j) * N + n] & 0xF) << (8 * j);"),
+    # 4-bit activations (W4A4)
+    "a4_divisor_eight": ("const float sa = amax / 7.0f;", "const float sa = amax / 8.0f;"),
+    "a4_amax_signed": ("amax = fmaxf(amax, fabsf((float)oracle_bf16_to_f64(A[m * K + k])));",
+                       "amax = fmaxf(amax, (float)oracle_bf16_to_f64(A[m * K + k]));"),
+    "a4_ties_away": ("fmaxf(rintf(a / sa), -8.0f)", "fmaxf(roundf(a / sa), -8.0f)"),
+    "a4_truncate": ("fmaxf(rintf(a / sa), -8.0f)", "fmaxf(truncf(a / sa), -8.0f)"),
+    "a4_offset_seven": ("(uint32_t)(qa + 8) << (4 * (k % 8))", "(uint32_t)(qa + 7) << (4 * (k % 8))"),
+    "a4_decode_offset_seven": ("& 0xFu) - 8;", "& 0xFu) - 7;"),
+    "a4_nibble_order": ("(Aq[m * (K / 8) + k / 8] >> (4 * (k % 8)))", "(Aq[m * (K / 8) + k / 8] >> (4 * (7 - k % 8)))"),
+    "a4_scale_wrong_group": ("(double)As[m * G + gk]", "(double)As[m * G + (gk + 1) % G]"),
+    "a4_scale_wrong_row": ("(double)As[m * G + gk]", "(double)As[((m + 1) % M) * G + gk]"),
+    "a4_weight_zero_dropped": ("(oracle_code(Wq, N, k, n) - (Z[gk * N + n] & 0xF))", "(oracle_code(Wq, N, k, n))"),
+    "a4_abs_signed": ("magnitude += fabs(term);", "magnitude += term;"),
+    "a4_activation_row_swapped": ("oracle_act_code(Aq, K, m, k)", "oracle_act_code(Aq, K, (m + 1) % M, k)"),
 }
 
 
