@@ -132,6 +132,9 @@ def main():
             d["Wq"] = torch.from_numpy(x.Wq.view(np.int32)).to(dev)
         else:
             d["Wq"] = w4.pack(torch.from_numpy(x.q).to(dev), bits=spec.bits)
+        if spec.act4:  # 4-bit activations in place of the bfloat16 ones
+            d["A"] = torch.from_numpy(x.Aq.view(np.int32)).to(dev)
+            d["As"] = torch.from_numpy(x.As).to(dev)
         d["C"] = torch.empty((spec.M, spec.N), dtype=torch.float32, device=dev)
         gemms.append((spec, d))
         if not args.no_cpu_baseline:
@@ -144,7 +147,9 @@ def main():
     handle = stream.cuda_stream
     lib = w4.lib()
     # each GEMM through the C-ABI entry point of its code width
-    calls = [(lib.w8a16_gemm if spec.bits == 8 else lib.w4a16_gemm,
+    calls = [(lib.w4a4_gemm, (d["A"].data_ptr(), d["As"].data_ptr(), d["Wq"].data_ptr(), d["S"].data_ptr(),
+                              d["Z"].data_ptr(), d["C"].data_ptr(), spec.M, spec.K, spec.N)) if spec.act4 else
+             (lib.w8a16_gemm if spec.bits == 8 else lib.w4a16_gemm,
               (d["A"].data_ptr(), d["Wq"].data_ptr(), d["S"].data_ptr(), d["Z"].data_ptr(), d["C"].data_ptr(),
                spec.M, spec.K, spec.N)) for spec, d in gemms]
 
@@ -209,7 +214,7 @@ def main():
     # flops) per launch are the step's totals divided by the same count.
     launches = args.steps * len(calls)
     avg_dur_s = elapsed_ms * 1e-3 / launches
-    kinds = [w4.plan(spec.M, spec.K, spec.N, bits=spec.bits)["kernel"] for spec, _ in gemms]
+    kinds = [w4.plan(spec.M, spec.K, spec.N, bits=spec.bits, a4=spec.act4)["kernel"] for spec, _ in gemms]
     large_bytes = sum(spec.weight_bytes for (spec, _), k in zip(gemms, kinds) if k == 3)
     kernel = KERNEL_NAME_LARGE if 2 * large_bytes > wl.weight_bytes else KERNEL_NAME
     dtype = "bf16" if all(k == 3 for k in kinds) else ("f16" if all(k != 3 for k in kinds) else "f16+bf16")
@@ -279,7 +284,10 @@ def main():
         while time.perf_counter() - t1 < CPU_SAMPLE_SECONDS:
             spec, x = host_sample[done % len(host_sample)]
             Wq = x.Wq if x.Wq is not None else (orc.pack8(x.q) if spec.bits == 8 else orc.pack(x.q))
-            orc.gemm(x.A, Wq, x.S, x.Z, threads=threads, bits=spec.bits)
+            if spec.act4:
+                orc.gemm_a4(x.Aq, x.As, Wq, x.S, x.Z, threads=threads)
+            else:
+                orc.gemm(x.A, Wq, x.S, x.Z, threads=threads, bits=spec.bits)
             nbytes += spec.weight_bytes
             done += 1
         dt = time.perf_counter() - t1

@@ -91,6 +91,37 @@ w4_status w8a16_gemm(const void *A_bf16, const uint32_t *Wq8, const void *scales
                      void *stream);
 
 /*
+ * C = A . W with 4-bit activations on the 4-bit weights (W4A4): the draft side of QSPEC's
+ * complementary scheme, which "When Do Quantized Drafts Help Speculative Decoding?" ("What
+ * is open") describes as a W4A4 draft verified by W4A16 on the same weights.  The pages
+ * print no activation format; this is the plainest reading, symmetric per row and group of
+ * 128 along K (as produced by a4_quantize):
+ *     Aq         [M, K/8]    uint32; nibble j of Aq[m,kb] is qa[m, 8kb+j] + 8, qa in -8..7
+ *     A_scales   [M, K/128]  float32 sa
+ *     Wq, scales_f16, zeros_u4: the 4-bit weight format of w4a16_gemm
+ *     C[m,n] = sum_g sa[m,g] * s[g,n] * sum_{k in g} qa[m,k] * (q[k,n] - z[g,n])
+ *   Aq and A_scales 4-byte aligned; Wq and C 16-byte aligned; scales_f16 2-byte.  Sizes,
+ *   workspace, stream and errors as for w4a16_gemm.  Each group's inner sum is an exact
+ *   integer; it is scaled by sa * s in float32, so every element is within
+ *   1e-4 * sum_k |sa qa (q - z) s| + 1e-6 of the exact value.  Every M runs on the binary16
+ *   matrix cores in row blocks of 16.
+ */
+w4_status w4a4_gemm(const uint32_t *Aq, const float *A_scales, const uint32_t *Wq, const void *scales_f16,
+                    const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N, void *stream);
+
+/*
+ * The activation quantizer of w4a4_gemm: for each row m and group g of 128 along K,
+ *     amax = max |A[m,k]|,  sa = amax / 7,  qa = clamp(rint(A / sa), -8, 7)  (0 if sa == 0)
+ * every step in binary32 with IEEE division and rint ties to even, so the codes are
+ * reproducible bit for bit.
+ *   A_bf16:   [M, K] bfloat16, 16-byte aligned (not modified); inputs must be finite.
+ *   Aq:       [M, K/8] uint32, 4-byte aligned, overwritten (nibble j = qa[8kb+j] + 8).
+ *   A_scales: [M, K/128] float32, 4-byte aligned, overwritten.
+ *   M >= 1, K >= 128, K % 128 == 0.  Asynchronous on `stream`; errors as for w4a16_gemm.
+ */
+w4_status a4_quantize(const void *A_bf16, uint32_t *Aq, float *A_scales, int64_t M, int64_t K, void *stream);
+
+/*
  * Packs 8-bit codes into the 8-bit storage layout: Wq8[kb,n] = sum_j q[4kb+j,n] << 8j.
  *   q_u8: [K, N] bytes; Wq8: [K/4, N] uint32, overwritten.
  *   K >= 4 with K % 4 == 0, N >= 1; Wq8 must be 4-byte aligned.  Bit-exact.
@@ -148,15 +179,16 @@ typedef struct w4_plan {
                                2 = small-M tall (12 waves, fp16 MFMA),
                                3 = large-M (M >= 64, or M >= 17 with K*N >= 2^25:
                                    8 waves, bf16 MFMA),
-                               4, 5 = 8-bit codes (w8a16_gemm), wide and tall as 1, 2       */
-    int tile_m;             /* output rows per row block (16 for kernels 1, 2, 4, 5; 1 to
+                               4, 5 = 8-bit codes (w8a16_gemm), wide and tall as 1, 2,
+                               6, 7 = 4-bit activations (w4a4_gemm), wide and tall          */
+    int tile_m;             /* output rows per row block (16 for kernels 1, 2, 4 to 7; 1 to
                                160 for kernel 3, computed in row tiles of 32)                */
     int tile_n;             /* output columns per workgroup tile (64, or 256 for kernel 3)   */
     int m_blocks;           /* row blocks of tile_m                                          */
     int n_tiles;            /* column tiles of tile_n                                        */
     int splits;             /* K splits across workgroups (1 = no workspace)                */
     int groups_per_split;   /* 128-wide K groups handled by one workgroup of a split tile    */
-    int full_tiles;         /* kernels 1, 4: tiles 0..full_tiles-1 (row-block-major order) run
+    int full_tiles;         /* kernels 1, 4, 6: tiles 0..full_tiles-1 (row-block-major order) run
                                unsplit, one workgroup each, and only the other tiles are
                                split (a multiple of 256: whole rounds of CUs); 0 otherwise  */
     int64_t workgroups;     /* grid size: full_tiles + (m_blocks*n_tiles - full_tiles)*splits */
@@ -167,6 +199,9 @@ w4_status w4a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out);
 
 /* How w8a16_gemm would run a shape (host only, no HIP call). */
 w4_status w8a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out);
+
+/* How w4a4_gemm would run a shape (host only, no HIP call). */
+w4_status w4a4_plan(int64_t M, int64_t K, int64_t N, w4_plan *out);
 
 /* Static text for a status code. */
 const char *w4_status_string(w4_status s);

@@ -89,6 +89,12 @@ _lib.w8_pack.argtypes = [_vp, _vp, _i64, _i64, _vp]
 _lib.w8_pack.restype = ctypes.c_int
 _lib.w8a16_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(Plan)]
 _lib.w8a16_plan.restype = ctypes.c_int
+_lib.w4a4_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+_lib.w4a4_gemm.restype = ctypes.c_int
+_lib.w4a4_plan.argtypes = [_i64, _i64, _i64, ctypes.POINTER(Plan)]
+_lib.w4a4_plan.restype = ctypes.c_int
+_lib.a4_quantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp]
+_lib.a4_quantize.restype = ctypes.c_int
 _lib.w4_status_string.argtypes = [ctypes.c_int]
 _lib.w4_status_string.restype = ctypes.c_char_p
 _lib.w4_last_error.argtypes = []
@@ -104,7 +110,7 @@ def header_functions(path: str = HEADER) -> List[str]:
     with open(path) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\**\s*\b(w[48]\w*)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\**\s*\b((?:w[48]|a4)\w*)\s*\(", text, flags=re.M)
 
 
 def status_string(code: int) -> str:
@@ -119,9 +125,10 @@ def _bits_fns(bits: int):
     raise ValueError("bits must be 4 or 8")
 
 
-def plan(M: int, K: int, N: int, bits: int = 4) -> Dict[str, int]:
-    """How the GEMM entry point for `bits`-wide codes would run a shape (host only)."""
-    fn, name = _bits_fns(bits)[4:]
+def plan(M: int, K: int, N: int, bits: int = 4, a4: bool = False) -> Dict[str, int]:
+    """How the GEMM entry point for `bits`-wide codes (or, with a4, w4a4_gemm) would run a
+    shape (host only)."""
+    fn, name = (_lib.w4a4_plan, "w4a4_plan") if a4 else _bits_fns(bits)[4:]
     p = Plan()
     rc = fn(M, K, N, ctypes.byref(p))
     if rc:
@@ -178,6 +185,50 @@ def gemm(A, Wq, scales, zeros, out=None, stream=None, bits: int = 4):
             out.data_ptr(), M, K, N, _stream_handle(stream))
     if rc:
         raise W4Error(rc, name)
+    return out
+
+
+def quantize_activations(A, stream=None):
+    """4-bit activations: bfloat16 A [M, K] -> (Aq int32 [M, K/8] offset-binary codes,
+    A_scales float32 [M, K/128]), symmetric per row and group of 128 (a4_quantize)."""
+    import torch
+    _check(A, "A", torch.bfloat16, 2)
+    M, K = A.shape
+    Aq = torch.empty((M, K // 8), dtype=torch.int32, device=A.device)
+    As = torch.empty((M, K // 128), dtype=torch.float32, device=A.device)
+    rc = _lib.a4_quantize(A.data_ptr(), Aq.data_ptr(), As.data_ptr(), M, K, _stream_handle(stream))
+    if rc:
+        raise W4Error(rc, "a4_quantize")
+    return Aq, As
+
+
+def gemm_a4(Aq, A_scales, Wq, scales, zeros, out=None, stream=None):
+    """W4A4: C[M,N] from 4-bit activations (Aq int32 [M, K/8], A_scales float32 [M, K/128])
+    and the 4-bit weight format (Wq int32 [K/8, N], scales float16, zeros uint8)."""
+    import torch
+    for t, name in ((Aq, "Aq"), (Wq, "Wq")):
+        if t.dtype not in (torch.int32, torch.uint32):
+            raise TypeError(f"{name} must be int32 or uint32")
+        _check(t, name, t.dtype, 2)
+    _check(A_scales, "A_scales", torch.float32, 2)
+    _check(scales, "scales", torch.float16, 2)
+    _check(zeros, "zeros", torch.uint8, 2)
+    M, K = Aq.shape[0], Aq.shape[1] * 8
+    N = Wq.shape[1]
+    if (Wq.shape[0] * 8 != K or A_scales.shape != (M, K // 128) or scales.shape != (K // 128, N)
+            or zeros.shape != (K // 128, N)):
+        raise ValueError(f"inconsistent shapes Aq{tuple(Aq.shape)} A_scales{tuple(A_scales.shape)} "
+                         f"Wq{tuple(Wq.shape)} scales{tuple(scales.shape)} zeros{tuple(zeros.shape)}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=Aq.device)
+    else:
+        _check(out, "out", torch.float32, 2)
+        if tuple(out.shape) != (M, N):
+            raise ValueError("out has the wrong shape")
+    rc = _lib.w4a4_gemm(Aq.data_ptr(), A_scales.data_ptr(), Wq.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                        out.data_ptr(), M, K, N, _stream_handle(stream))
+    if rc:
+        raise W4Error(rc, "w4a4_gemm")
     return out
 
 

@@ -76,7 +76,7 @@ constexpr Variant kTall = {12, 1};
 constexpr int kOccupancy = 3;  // waves per SIMD: at most 168 VGPRs per lane
 
 struct SmallParams {
-    const uint16_t *A;
+    const uint16_t *A;  // bfloat16 [M, K]; with 4-bit activations the packed codes [M, K/8]
     const uint32_t *Wq;
     const uint16_t *S;
     const uint8_t *Z;
@@ -86,6 +86,7 @@ struct SmallParams {
     int64_t M, K, N;
     int groups, splits, gps, n_tiles, m_blocks;
     int full_tiles;     // tiles [0, full_tiles) are not split (a multiple of 8)
+    const float *As;    // 4-bit activations only: float32 scales [M, K/128]
 };
 
 // ------------------------------------------------------------------------------------
@@ -226,7 +227,7 @@ struct LaneOffsets {
 };
 
 struct Resources {
-    __amdgpu_buffer_rsrc_t W, S, Z, A;
+    __amdgpu_buffer_rsrc_t W, S, Z, A, As;
 };
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit dwords
@@ -293,26 +294,35 @@ __device__ __forceinline__ void load_group(const SmallParams &p, const Resources
 // chunks travel in the register ring with the group's weights, so the conversion overlaps
 // the loads still in flight and there is no workgroup-wide staging phase.
 
-template <int AV, int BITS>
+template <int AV, int BITS, bool A4>
 struct PipeRegs {
     u32x4 w[BITS];
     u32x2 s;      // 4 binary16 scales
     uint32_t z;   // 4 zero bytes
-    u32x4 a[AV];  // activation chunks: rows 4i + lane/16, chunk lane%16 of the group
+    // activation chunks of rows 4i + lane/16, chunk lane%16 of the group: 8 bfloat16
+    // values, or (4-bit activations) one word of 8 codes and the row's scale bits
+    typename std::conditional<A4, u32x2, u32x4>::type a[AV];
 };
 
 constexpr int kPipeWaveBytes = kTileM * kARowBytes + kTileM * 4;  // tile + row exponents
 constexpr int kPipeExpOffset = kTileM * kARowBytes;
 
-template <bool VEC, int AV, int BITS>
+template <bool VEC, int AV, int BITS, bool A4>
 __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources &rs, const LaneOffsets<VEC> &o,
-                                          const uint32_t (&aoff)[AV], int g, PipeRegs<AV, BITS> &r)
+                                          const uint32_t (&aoff)[AV], const uint32_t (&asoff)[AV], int g,
+                                          PipeRegs<AV, BITS, A4> &r)
 {
     // activations first: their conversion needs only them, and can run while the
     // weights are still in flight (loads complete in issue order)
 #pragma unroll
-    for (int i = 0; i < AV; ++i)
-        r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[i], (uint32_t)g * (kGroup * 2), 0);
+    for (int i = 0; i < AV; ++i) {
+        if constexpr (A4) {
+            r.a[i].x = __builtin_amdgcn_raw_buffer_load_b32(rs.A, aoff[i], (uint32_t)g * (kGroup / 2), 0);
+            r.a[i].y = __builtin_amdgcn_raw_buffer_load_b32(rs.As, asoff[i], (uint32_t)g * 4, 0);
+        } else {
+            r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[i], (uint32_t)g * (kGroup * 2), 0);
+        }
+    }
     GroupRegs<BITS> w;
     load_group<VEC, BITS>(p, rs, o, g, w);
 #pragma unroll
@@ -323,25 +333,40 @@ __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources 
 
 // Convert this wave's group of activations into its LDS tile: row r scaled by 2^x[r],
 // x[r] = 142 - (largest biased exponent of row r in the group); exponents stored next to
-// the tile.  The 16 chunks of a row sit in 16 consecutive lanes.
-template <int AV, int BITS>
-__device__ __forceinline__ void stage_pipe(const PipeRegs<AV, BITS> &r, char *lds_wave, int mv, int lane)
+// the tile.  The 16 chunks of a row sit in 16 consecutive lanes.  4-bit activations are
+// unpacked instead (offset-binary codes, zero point 8, exact in binary16, in the weight
+// operand's element order) and the row's float32 scale is stored in place of x[r].
+template <int AV, int BITS, bool A4>
+__device__ __forceinline__ void stage_pipe(const PipeRegs<AV, BITS, A4> &r, char *lds_wave, int mv, int lane)
 {
     asm volatile("" ::: "memory");  // the previous group's LDS reads stay before these writes
     const int kc = lane & 15;
+    if constexpr (A4) {
+        uint32_t magic, zlo = (0xE400u | 8u) * 0x00010001u, zhi = (0xD400u | (8u << 4)) * 0x00010001u;
+        asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+        asm volatile("" : "+v"(zlo), "+v"(zhi));
 #pragma unroll
-    for (int i = 0; i < AV; ++i) {
-        const int row = 4 * i + (lane >> 4);
-        const int e = row16_max(chunk_max_exp(r.a[i]));
-        const int x = 142 - max(e, 1);
-        if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = convert_chunk<BITS>(r.a[i], x);
-        if (kc == 0) *(int *)(lds_wave + kPipeExpOffset + 4 * row) = row < mv ? x : 0;
+        for (int i = 0; i < AV; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            const f16x8 v = unpack8(r.a[i].x, zlo, zhi, magic);
+            if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = __builtin_bit_cast(u32x4, v);
+            if (kc == 0) *(uint32_t *)(lds_wave + kPipeExpOffset + 4 * row) = row < mv ? r.a[i].y : 0u;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < AV; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            const int e = row16_max(chunk_max_exp(r.a[i]));
+            const int x = 142 - max(e, 1);
+            if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = convert_chunk<BITS>(r.a[i], x);
+            if (kc == 0) *(int *)(lds_wave + kPipeExpOffset + 4 * row) = row < mv ? x : 0;
+        }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's tile is complete
 }
 
-template <int AV, int BITS>
-__device__ __forceinline__ void compute_pipe(const PipeRegs<AV, BITS> &r, const char *lds_wave, int mv, int lane,
+template <int AV, int BITS, bool A4>
+__device__ __forceinline__ void compute_pipe(const PipeRegs<AV, BITS, A4> &r, const char *lds_wave, int mv, int lane,
                                              f32x4 (&acc)[4])
 {
     const int c = lane & 15, kq = lane >> 4;
@@ -392,18 +417,31 @@ __device__ __forceinline__ void compute_pipe(const PipeRegs<AV, BITS> &r, const 
             }
         }
     }
-    const int4 xr = *(const int4 *)(lds_wave + kPipeExpOffset + 16 * kq);
-    const int xs[4] = {xr.x, xr.y, xr.z, xr.w};
+    if constexpr (A4) {
+        // the group's partials are exact integers; each is scaled by its row's activation
+        // scale times its column's weight scale
+        const f32x4 sa = *(const f32x4 *)(lds_wave + kPipeExpOffset + 16 * kq);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
-        const float sv = (float)__builtin_bit_cast(_Float16, sb);
+        for (int t = 0; t < 4; ++t) {
+            const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
+            const float sv = (float)__builtin_bit_cast(_Float16, sb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(ldexpf(sv, -xs[i]), P[t][i], acc[t][i]);
+            for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(sv * sa[i], P[t][i], acc[t][i]);
+        }
+    } else {
+        const int4 xr = *(const int4 *)(lds_wave + kPipeExpOffset + 16 * kq);
+        const int xs[4] = {xr.x, xr.y, xr.z, xr.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
+            const float sv = (float)__builtin_bit_cast(_Float16, sb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(ldexpf(sv, -xs[i]), P[t][i], acc[t][i]);
+        }
     }
 }
 
-template <bool VEC, int WAVES, int AV, int OCC, int BITS>
+template <bool VEC, int WAVES, int AV, int OCC, int BITS, bool A4>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void w4a16_kernel(SmallParams p)
 {
@@ -445,15 +483,23 @@ void w4a16_kernel(SmallParams p)
     rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K * BITS / 32 * p.N * 4), kRsrcWord3);
     rs.S = __builtin_amdgcn_make_buffer_rsrc((void *)p.S, (short)0, (int)(p.K / kGroup * p.N * 2), kRsrcWord3);
     rs.Z = __builtin_amdgcn_make_buffer_rsrc((void *)p.Z, (short)0, (int)(p.K / kGroup * p.N), kRsrcWord3);
-    rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(p.M * p.K * 2), kRsrcWord3);
+    rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(A4 ? p.M * p.K / 2 : p.M * p.K * 2), kRsrcWord3);
+    if constexpr (A4)
+        rs.As = __builtin_amdgcn_make_buffer_rsrc((void *)p.As, (short)0, (int)(p.M * (p.K / kGroup) * 4), kRsrcWord3);
     LaneOffsets<VEC> lo;
     lane_offsets<VEC, BITS>(p, n0, lane, lo);
-    uint32_t aoff[AV];
+    uint32_t aoff[AV], asoff[AV];
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
         int row = 4 * i + (lane >> 4);
         row = row < mv ? row : mv - 1;
-        aoff[i] = (uint32_t)(((int64_t)(m0 + row) * p.K + (lane & 15) * 8) * 2);
+        if constexpr (A4) {
+            aoff[i] = (uint32_t)(((int64_t)(m0 + row) * (p.K / 8) + (lane & 15)) * 4);
+            asoff[i] = (uint32_t)((int64_t)(m0 + row) * (p.K / kGroup) * 4);
+        } else {
+            aoff[i] = (uint32_t)(((int64_t)(m0 + row) * p.K + (lane & 15) * 8) * 2);
+            asoff[i] = 0;
+        }
     }
     // rows 4*AV..15 of this wave's exponent table are never staged: they read as 0; rows
     // mv..15 of its activation tile are never staged either: they read as 0 in the MFMAs
@@ -468,22 +514,22 @@ void w4a16_kernel(SmallParams p)
     // Two register slots: group j+1 (weights and activations) is in flight while group j is
     // converted and computed.
     auto G = [&](int j) { return g0 + WAVES * j; };
-    auto run = [&](const PipeRegs<AV, BITS> &r) {
-        stage_pipe<AV, BITS>(r, tile_lds, mv, lane);
-        compute_pipe<AV, BITS>(r, tile_lds, mv, lane, acc);
+    auto run = [&](const PipeRegs<AV, BITS, A4> &r) {
+        stage_pipe<AV, BITS, A4>(r, tile_lds, mv, lane);
+        compute_pipe<AV, BITS, A4>(r, tile_lds, mv, lane, acc);
     };
     if (n_my > 0) {
-        PipeRegs<AV, BITS> r0, r1;
-        load_pipe<VEC, AV, BITS>(p, rs, lo, aoff, G(0), r0);
+        PipeRegs<AV, BITS, A4> r0, r1;
+        load_pipe<VEC, AV, BITS, A4>(p, rs, lo, aoff, asoff, G(0), r0);
         int j = 0;
         for (; j + 2 < n_my; j += 2) {
-            load_pipe<VEC, AV, BITS>(p, rs, lo, aoff, G(j + 1), r1);
+            load_pipe<VEC, AV, BITS, A4>(p, rs, lo, aoff, asoff, G(j + 1), r1);
             run(r0);
-            load_pipe<VEC, AV, BITS>(p, rs, lo, aoff, G(j + 2), r0);
+            load_pipe<VEC, AV, BITS, A4>(p, rs, lo, aoff, asoff, G(j + 2), r0);
             run(r1);
         }
         if (j + 1 < n_my) {
-            load_pipe<VEC, AV, BITS>(p, rs, lo, aoff, G(j + 1), r1);
+            load_pipe<VEC, AV, BITS, A4>(p, rs, lo, aoff, asoff, G(j + 1), r1);
             run(r0);
             run(r1);
         } else {
@@ -833,6 +879,43 @@ __global__ __launch_bounds__(256) void w4a16_split_reduce(const float *__restric
     }
 }
 
+// 4-bit activation quantizer: one (row, 128-wide group) per 16 lanes (a DPP row), each lane
+// holding 8 consecutive values (one 16-byte load) and producing their packed word.
+//   amax = max |A| over the group (the largest magnitude bit pattern: the order of
+//          non-negative floats is that of their bits), sa = amax / 7 (IEEE division),
+//   qa = clamp(rint(A / sa), -8, 7) (IEEE division, ties to even), 0 when sa == 0,
+//   nibble j of the word = qa[8 kc + j] + 8.
+__global__ __launch_bounds__(256) void a4_quantize_kernel(const uint16_t *__restrict__ A, uint32_t *__restrict__ Aq,
+                                                          float *__restrict__ As, int64_t units, int groups)
+{
+    const int64_t unit = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int kc = threadIdx.x & 15;
+    const bool live = unit < units;  // the whole DPP row shares `unit`, so rows are live or dead as one
+    const int64_t u = live ? unit : units - 1;
+    const u32x4 v = *(const u32x4 *)(A + u * kGroup + kc * 8);  // row-major [M, K]: unit = m * groups + g
+    int mag = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        mag = max(mag, (int)(v[j] & 0x7FFFu));
+        mag = max(mag, (int)((v[j] >> 16) & 0x7FFFu));
+    }
+    mag = row16_max(mag);
+    const float amax = __builtin_bit_cast(float, (uint32_t)mag << 16);
+    const float sa = amax / 7.0f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t bits = (j & 1) ? (v[j >> 1] & 0xFFFF0000u) : (v[j >> 1] << 16);
+        const float a = __builtin_bit_cast(float, bits);
+        const int qa = sa == 0.0f ? 0 : (int)fminf(fmaxf(rintf(a / sa), -8.0f), 7.0f);
+        word |= (uint32_t)(qa + 8) << (4 * j);
+    }
+    if (live) {
+        Aq[u * 16 + kc] = word;
+        if (kc == 0) As[u] = sa;
+    }
+}
+
 // 8-bit codes: Wq8[kb,n] = sum_j q[4kb+j,n] << 8j, one word per thread.
 __global__ __launch_bounds__(256) void w8_pack_kernel(const uint8_t *__restrict__ q,
                                                       uint32_t *__restrict__ Wq8, int64_t KB, int64_t N)
@@ -1112,7 +1195,7 @@ w4_status get_workspace(int dev, hipStream_t stream, size_t tiles, size_t part_b
     return W4_OK;
 }
 
-w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N, int bits = 4)
+w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N, int bits = 4, bool a4 = false)
 {
     if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) {
         set_error("shape M=%lld K=%lld N=%lld: need M>=1, N>=1, K>=128, K%%128==0",
@@ -1120,7 +1203,7 @@ w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N, int bits = 4)
         return W4_ERR_SHAPE;
     }
     // the kernels address each array with 32-bit byte offsets
-    if (K * bits / 32 * N * 4 >= ((int64_t)1 << 31) || M * K * 2 >= ((int64_t)1 << 31)) {
+    if (K * bits / 32 * N * 4 >= ((int64_t)1 << 31) || M * K * (a4 ? 1 : 4) / 2 >= ((int64_t)1 << 31)) {
         set_error("shape M=%lld K=%lld N=%lld: packed weights or activations exceed 2 GiB",
                   (long long)M, (long long)K, (long long)N);
         return W4_ERR_SHAPE;
@@ -1255,10 +1338,14 @@ void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->workspace_bytes = best_s > 1 ? best_s * ((M * N + 3) / 4 * 4) * 4 : 0;
 }
 
-// Kernel ids of the small-M shapes: 1 / 2 (4-bit codes, wide / tall), 4 / 5 (8-bit codes).
-int small_kernel_id(bool tall, int bits) { return (bits == 8 ? 3 : 0) + (tall ? 2 : 1); }
+// Kernel ids of the small-M shapes: 1 / 2 (4-bit codes, wide / tall), 4 / 5 (8-bit codes),
+// 6 / 7 (4-bit codes and 4-bit activations).
+int small_kernel_id(bool tall, int bits, bool a4)
+{
+    return (a4 ? 5 : bits == 8 ? 3 : 0) + (tall ? 2 : 1);
+}
 
-void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4)
+void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4, bool a4 = false)
 {
     const int groups = (int)(K / kGroup);
     const int n_tiles = (int)((N + kTileN - 1) / kTileN);
@@ -1296,7 +1383,7 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4)
     const int gps = (groups + best.splits - 1) / best.splits;
     const int splits = (groups + gps - 1) / gps;
     const int64_t split_tiles = splits > 1 ? base - full : 0;
-    pl->kernel = small_kernel_id(best.v == &kTall, bits);
+    pl->kernel = small_kernel_id(best.v == &kTall, bits, a4);
     pl->tile_m = kTileM;
     pl->tile_n = kTileN;
     pl->m_blocks = m_blocks;
@@ -1321,7 +1408,7 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 size_t plan_lds_bytes(int64_t M, const w4_plan &pl)
 {
     const int rows = M < kTileM ? (int)M : kTileM;
-    const Variant &v = (pl.kernel == 2 || pl.kernel == 5) ? kTall : kWide;
+    const Variant &v = (pl.kernel == 2 || pl.kernel == 5 || pl.kernel == 7) ? kTall : kWide;
     const size_t tiles = (size_t)v.waves * kPipeWaveBytes;
     const size_t red = (size_t)v.waves * rows * kTileN * 4;
     return tiles > red ? tiles : red;
@@ -1329,11 +1416,11 @@ size_t plan_lds_bytes(int64_t M, const w4_plan &pl)
 
 // Small-M launches: one instantiation per (vectorized loads, waves, activation chunks per
 // lane, code width); every shape keeps 3 waves per SIMD.
-template <int BITS, int WAVES>
+template <int BITS, int WAVES, bool A4>
 void launch_small(int av, bool vec, dim3 grid, size_t lds, hipStream_t s, const SmallParams &p)
 {
 #define W4_LAUNCH(V, AVV) \
-    hipLaunchKernelGGL((w4a16_kernel<V, WAVES, AVV, kOccupancy, BITS>), grid, dim3(WAVES * kWave), lds, s, p)
+    hipLaunchKernelGGL((w4a16_kernel<V, WAVES, AVV, kOccupancy, BITS, A4>), grid, dim3(WAVES * kWave), lds, s, p)
 #define W4_LAUNCH_AV(V) \
     switch (av) { case 1: W4_LAUNCH(V, 1); break; case 2: W4_LAUNCH(V, 2); break; \
                   case 3: W4_LAUNCH(V, 3); break; default: W4_LAUNCH(V, 4); break; }
@@ -1342,18 +1429,25 @@ void launch_small(int av, bool vec, dim3 grid, size_t lds, hipStream_t s, const 
 #undef W4_LAUNCH
 }
 
-// The GEMM for either code width: host validation, plan, workspace, launches.
-w4_status run_gemm(int bits, const char *name, const void *A_bf16, const uint32_t *Wq, const void *scales_f16,
-                   const uint8_t *zeros, float *C, int64_t M, int64_t K, int64_t N, void *stream)
+// The GEMM for every variant (code width, activation type): host validation, plan,
+// workspace, launches.  With 4-bit activations, A_bf16 is the packed codes and As their
+// scales.
+w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, const float *As, const uint32_t *Wq,
+                   const void *scales_f16, const uint8_t *zeros, float *C, int64_t M, int64_t K, int64_t N,
+                   void *stream)
 {
-    if (!A_bf16 || !Wq || !scales_f16 || !zeros || !C) {
+    if (!A_bf16 || (a4 && !As) || !Wq || !scales_f16 || !zeros || !C) {
         set_error("%s: a required pointer is NULL", name);
         return W4_ERR_NULL;
     }
-    w4_status st = validate_gemm_shape(M, K, N, bits);
+    w4_status st = validate_gemm_shape(M, K, N, bits, a4);
     if (st != W4_OK) return st;
-    if (!aligned(A_bf16, 16) || !aligned(Wq, 16) || !aligned(C, 16) || !aligned(scales_f16, 2)) {
-        set_error("%s: A, Wq and C must be 16-byte aligned and scales 2-byte aligned", name);
+    if (a4 ? (!aligned(A_bf16, 4) || !aligned(As, 4)) : !aligned(A_bf16, 16)) {
+        set_error(a4 ? "%s: Aq and A_scales must be 4-byte aligned" : "%s: A must be 16-byte aligned", name);
+        return W4_ERR_ALIGN;
+    }
+    if (!aligned(Wq, 16) || !aligned(C, 16) || !aligned(scales_f16, 2)) {
+        set_error("%s: Wq and C must be 16-byte aligned and scales 2-byte aligned", name);
         return W4_ERR_ALIGN;
     }
     int dev = -1;
@@ -1361,8 +1455,8 @@ w4_status run_gemm(int bits, const char *name, const void *A_bf16, const uint32_
     if (st != W4_OK) return st;
 
     w4_plan pl;
-    if (bits == 8)
-        make_small_plan(M, K, N, &pl, 8);
+    if (bits == 8 || a4)
+        make_small_plan(M, K, N, &pl, bits, a4);
     else
         make_plan(M, K, N, &pl);
     hipStream_t s = (hipStream_t)stream;
@@ -1414,6 +1508,7 @@ w4_status run_gemm(int bits, const char *name, const void *A_bf16, const uint32_
     } else {
         SmallParams p;
         p.A = (const uint16_t *)A_bf16;
+        p.As = As;
         p.Wq = Wq;
         p.S = (const uint16_t *)scales_f16;
         p.Z = zeros;
@@ -1433,13 +1528,16 @@ w4_status run_gemm(int bits, const char *name, const void *A_bf16, const uint32_
         const size_t lds = plan_lds_bytes(M, pl);
         const int rows = M < kTileM ? (int)M : kTileM;
         const int av = (rows + 3) / 4;
-        const bool tall = pl.kernel == 2 || pl.kernel == 5;
-        if (bits == 8) {
-            if (tall) launch_small<8, kTall.waves>(av, vec, grid, lds, s, p);
-            else launch_small<8, kWide.waves>(av, vec, grid, lds, s, p);
+        const bool tall = pl.kernel == 2 || pl.kernel == 5 || pl.kernel == 7;
+        if (a4) {
+            if (tall) launch_small<4, kTall.waves, true>(av, vec, grid, lds, s, p);
+            else launch_small<4, kWide.waves, true>(av, vec, grid, lds, s, p);
+        } else if (bits == 8) {
+            if (tall) launch_small<8, kTall.waves, false>(av, vec, grid, lds, s, p);
+            else launch_small<8, kWide.waves, false>(av, vec, grid, lds, s, p);
         } else {
-            if (tall) launch_small<4, kTall.waves>(av, vec, grid, lds, s, p);
-            else launch_small<4, kWide.waves>(av, vec, grid, lds, s, p);
+            if (tall) launch_small<4, kTall.waves, false>(av, vec, grid, lds, s, p);
+            else launch_small<4, kWide.waves, false>(av, vec, grid, lds, s, p);
         }
     }
     hipError_t e = hipGetLastError();
@@ -1483,14 +1581,62 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
                      const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N,
                      void *stream)
 {
-    return run_gemm(4, "w4a16_gemm", A_bf16, Wq, scales_f16, zeros_u4, C, M, K, N, stream);
+    return run_gemm(4, false, "w4a16_gemm", A_bf16, nullptr, Wq, scales_f16, zeros_u4, C, M, K, N, stream);
 }
 
 w4_status w8a16_gemm(const void *A_bf16, const uint32_t *Wq8, const void *scales_f16,
                      const uint8_t *zeros_u8, float *C, int64_t M, int64_t K, int64_t N,
                      void *stream)
 {
-    return run_gemm(8, "w8a16_gemm", A_bf16, Wq8, scales_f16, zeros_u8, C, M, K, N, stream);
+    return run_gemm(8, false, "w8a16_gemm", A_bf16, nullptr, Wq8, scales_f16, zeros_u8, C, M, K, N, stream);
+}
+
+w4_status w4a4_gemm(const uint32_t *Aq, const float *A_scales, const uint32_t *Wq, const void *scales_f16,
+                    const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N, void *stream)
+{
+    return run_gemm(4, true, "w4a4_gemm", Aq, A_scales, Wq, scales_f16, zeros_u4, C, M, K, N, stream);
+}
+
+w4_status w4a4_plan(int64_t M, int64_t K, int64_t N, w4_plan *out)
+{
+    if (!out) {
+        set_error("w4a4_plan: out is NULL");
+        return W4_ERR_NULL;
+    }
+    w4_status st = validate_gemm_shape(M, K, N, 4, true);
+    if (st != W4_OK) return st;
+    make_small_plan(M, K, N, out, 4, true);
+    return W4_OK;
+}
+
+w4_status a4_quantize(const void *A_bf16, uint32_t *Aq, float *A_scales, int64_t M, int64_t K, void *stream)
+{
+    if (!A_bf16 || !Aq || !A_scales) {
+        set_error("a4_quantize: a required pointer is NULL");
+        return W4_ERR_NULL;
+    }
+    if (M < 1 || K < kGroup || K % kGroup != 0 || M * K * 2 >= ((int64_t)1 << 40)) {
+        set_error("a4_quantize: shape M=%lld K=%lld: need M>=1, K>=128, K%%128==0", (long long)M, (long long)K);
+        return W4_ERR_SHAPE;
+    }
+    if (!aligned(A_bf16, 16) || !aligned(Aq, 4) || !aligned(A_scales, 4)) {
+        set_error("a4_quantize: A must be 16-byte aligned, Aq and A_scales 4-byte aligned");
+        return W4_ERR_ALIGN;
+    }
+    int dev = -1;
+    w4_status st = check_device(&dev);
+    if (st != W4_OK) return st;
+    const int64_t units = M * (K / kGroup);
+    const int64_t blocks = (units + 15) / 16;
+    if (blocks > 0x7FFFFFFF) {
+        set_error("a4_quantize: shape M=%lld K=%lld is too large", (long long)M, (long long)K);
+        return W4_ERR_SHAPE;
+    }
+    hipLaunchKernelGGL(a4_quantize_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       (const uint16_t *)A_bf16, Aq, A_scales, units, (int)(K / kGroup));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("a4_quantize launch", e);
+    return W4_OK;
 }
 
 w4_status w8a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out)

@@ -14,7 +14,8 @@ import int4_weight_only_gemm_amd as w4
 def test_library_exports_every_declared_symbol():
     names = w4.header_functions()
     assert set(names) >= {"w4a16_gemm", "w4_pack", "w4a16_plan", "w4_status_string", "w4_last_error",
-                          "w8a16_gemm", "w8_pack", "w8a16_plan", "w4_quantize", "w4_read_probe"}
+                          "w8a16_gemm", "w8_pack", "w8a16_plan", "w4_quantize", "w4_read_probe",
+                          "w4a4_gemm", "w4a4_plan", "a4_quantize"}
     lib = w4.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in include/w4a16.h but not exported"
@@ -68,6 +69,41 @@ def test_packed_weight_limit_follows_code_width():
     (A16, W16, S8 + 1, Z4, C16)])
 def test_misaligned(ptrs, which):
     assert GEMMS[which](*ptrs, 5, 128, 64, None) == 3
+
+
+AS4 = 0x60000  # activation scales (never dereferenced)
+
+
+@pytest.mark.parametrize("ptrs", [
+    (None, AS4, W16, S8, Z4, C16), (A16, None, W16, S8, Z4, C16), (A16, AS4, None, S8, Z4, C16),
+    (A16, AS4, W16, None, Z4, C16), (A16, AS4, W16, S8, None, C16), (A16, AS4, W16, S8, Z4, None)])
+def test_w4a4_null_pointers(ptrs):
+    assert w4.lib().w4a4_gemm(*ptrs, 5, 128, 64, None) == 1
+
+
+@pytest.mark.parametrize("mkn", [(0, 128, 64), (5, 64, 64), (5, 129, 64), (5, 128, 0), (1 << 31, 1 << 20, 1 << 20)])
+def test_w4a4_bad_shapes(mkn):
+    assert w4.lib().w4a4_gemm(A16, AS4, W16, S8, Z4, C16, *mkn, None) == 2
+
+
+@pytest.mark.parametrize("ptrs", [
+    (A16 + 2, AS4, W16, S8, Z4, C16), (A16, AS4 + 2, W16, S8, Z4, C16), (A16, AS4, W16 + 4, S8, Z4, C16),
+    (A16, AS4, W16, S8, Z4, C16 + 8), (A16, AS4, W16, S8 + 1, Z4, C16)])
+def test_w4a4_misaligned(ptrs):
+    assert w4.lib().w4a4_gemm(*ptrs, 5, 128, 64, None) == 3
+
+
+def test_a4_quantize_validation():
+    q = w4.lib().a4_quantize
+    assert q(None, W16, AS4, 2, 128, None) == 1
+    assert q(A16, None, AS4, 2, 128, None) == 1
+    assert q(A16, W16, None, 2, 128, None) == 1
+    assert q(A16, W16, AS4, 0, 128, None) == 2
+    assert q(A16, W16, AS4, 2, 64, None) == 2
+    assert q(A16, W16, AS4, 2, 200, None) == 2
+    assert q(A16 + 8, W16, AS4, 2, 128, None) == 3
+    assert q(A16, W16 + 2, AS4, 2, 128, None) == 3
+    assert q(A16, W16, AS4 + 1, 2, 128, None) == 3
 
 
 def test_pack8_validation():
@@ -138,16 +174,19 @@ def test_plan_covers_shapes():
     # a balanced wide plan runs whole rounds of 256 tiles unsplit and splits the rest
     import synth
     seen = set()
-    shapes = [(g.M, g.K, g.N, g.bits) for wl in synth.WORKLOADS.values() for g in wl.gemms]
-    shapes += [(M, K, N, 8) for M in (1, 5, 16, 17, 40, 64, 160) for K, N in ((3584, 4608), (18944, 3584), (128, 3))]
+    shapes = [(g.M, g.K, g.N, g.bits, g.act4) for wl in synth.WORKLOADS.values() for g in wl.gemms]
+    shapes += [(M, K, N, bits, a4) for M in (1, 5, 16, 17, 40, 64, 160) for K, N in ((3584, 4608), (18944, 3584), (128, 3))
+               for bits, a4 in ((8, False), (4, True))]
     for key in shapes:
         if key in seen:
             continue
         seen.add(key)
-        M, K, N, bits = key
-        p = w4.plan(M, K, N, bits=bits)
+        M, K, N, bits, a4 = key
+        p = w4.plan(M, K, N, bits=bits, a4=a4)
         groups = K // 128
-        if bits == 8:  # every row count runs on the 8-bit small-M kernel
+        if a4:  # every row count runs on the 4-bit-activation small-M kernel
+            assert p["kernel"] in (6, 7)
+        elif bits == 8:  # every row count runs on the 8-bit small-M kernel
             assert p["kernel"] in (4, 5)
         else:
             assert (p["kernel"] == 3) == (M >= 64 or (M >= 17 and K * N >= 1 << 25))
@@ -163,11 +202,11 @@ def test_plan_covers_shapes():
             tiles = p["n_tiles"] * p["m_blocks"]
             full = p["full_tiles"]
             assert full % 256 == 0 and 0 <= full < tiles
-            assert full == 0 or (p["kernel"] in (1, 4) and p["splits"] > 1)
+            assert full == 0 or (p["kernel"] in (1, 4, 6) and p["splits"] > 1)
             assert p["workgroups"] == full + (tiles - full) * p["splits"]
             assert (p["workspace_bytes"] > 0) == (p["splits"] > 1)
-            if p["kernel"] in (1, 2, 4, 5):  # every workgroup resident at once
-                assert p["workgroups"] <= 256 * (3 if p["kernel"] in (1, 4) else 1) or p["splits"] == 1
+            if p["kernel"] != 3:  # every workgroup resident at once
+                assert p["workgroups"] <= 256 * (3 if p["kernel"] in (1, 4, 6) else 1) or p["splits"] == 1
     with pytest.raises(w4.W4Error):
         w4.plan(5, 100, 64)
 
