@@ -314,6 +314,7 @@ def main():
         "tflops": round(tflops, 3),
         "config": {
             "workload": args.workload,
+            "variant": "+".join(sorted({"w4a4" if s.act4 else f"w{s.bits}a16" for s, _ in gemms})),
             "gemms_per_step": len(gemms),
             "copies": args.copies,
             "M": sorted({s.M for s, _ in gemms}),
