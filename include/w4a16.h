@@ -188,7 +188,8 @@ typedef struct w4_plan {
     int n_tiles;            /* column tiles of tile_n                                        */
     int splits;             /* K splits across workgroups (1 = no workspace)                */
     int groups_per_split;   /* 128-wide K groups handled by one workgroup of a split tile    */
-    int full_tiles;         /* kernels 1, 4, 6: tiles 0..full_tiles-1 (row-block-major order) run
+    int full_tiles;         /* kernels 1, 4, 6: tiles 0..full_tiles-1 (tile t is row block
+                               t % m_blocks of column tile t / m_blocks) run
                                unsplit, one workgroup each, and only the other tiles are
                                split (a multiple of 256: whole rounds of CUs); 0 otherwise  */
     int64_t workgroups;     /* grid size: full_tiles + (m_blocks*n_tiles - full_tiles)*splits */

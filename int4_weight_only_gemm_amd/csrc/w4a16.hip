@@ -465,8 +465,10 @@ void w4a16_kernel(SmallParams p)
         gps = p.gps;
     }
     const bool split = tile >= nfull && p.splits > 1;
-    const int nt = (int)(tile % (uint32_t)p.n_tiles);
-    const int mb = (int)(tile / (uint32_t)p.n_tiles);
+    // Row blocks of one column tile are consecutive tiles, so they run side by side on one
+    // XCD and the second block's weight loads find the lines the first one brought in.
+    const int mb = (int)(tile % (uint32_t)p.m_blocks);
+    const int nt = (int)(tile / (uint32_t)p.m_blocks);
     const int n0 = nt * kTileN, m0 = mb * kTileM;
     const int mv = (p.M - m0 < kTileM) ? (int)(p.M - m0) : kTileM;
     const int lane = threadIdx.x & 63;
