@@ -1225,11 +1225,14 @@ w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N, int bits = 4, boo
 // where the per-wave compute is the groups a wave walks in turn times the time of one group
 // at the CU's wave count, the streaming rate is limited by the bytes the waves keep in
 // flight over the loaded latency (and by the achievable rate), and the handoff grows with
-// the number of partial tiles the last workgroup sums.  At (nearly) equal cost the shape
-// with more waves in flight wins.
+// the number of partial tiles the last workgroup sums.  A CU streams at most kGBsPerCU, so a
+// plan on few CUs is bounded by the bytes each of them pulls (8-bit weights at M=1 on 72 CUs:
+// 10.4 us measured, against 9.2 on 96 CUs and 7.9 on 144).  At (nearly) equal cost the
+// shape with more waves in flight wins.
 constexpr double kUsLaunch = 3.5;        // dispatch + first bytes from HBM
 constexpr double kUsLatency = 1.0;       // loaded latency seen by the in-flight bytes
 constexpr double kGBsPeak = 4500.0;      // achievable streaming rate of one launch
+constexpr double kGBsPerCU = 42.5;       // achievable streaming rate of one CU
 constexpr double kUsHandoff = 1.0;       // split-K: partial stores, arrival count
 constexpr double kUsPerSplit = 0.4;      // ... and reading back one partial tile
 constexpr double kUsPerGroup = 0.5;      // one group per wave, per wave resident on its SIMD
@@ -1258,7 +1261,11 @@ Choice score(const Variant &v, int64_t base, int groups, int splits, int av, int
     const double inflight = (double)wgs * active_waves_per_wg * (per_wave < 2 ? per_wave : 2) * group_bytes(bits);
     double rate = inflight / (kUsLatency * 1e-6) / 1e9;  // GB/s
     if (rate > kGBsPeak) rate = kGBsPeak;
-    const double stream = (double)K * N * (bits / 8.0 + 3.0 / kGroup) / (rate * 1e3);  // us
+    const double bytes = (double)K * N * (bits / 8.0 + 3.0 / kGroup);
+    const double busy_cus = (double)(wgs < kCUs ? wgs : kCUs);
+    double stream = bytes / (rate * 1e3);  // us
+    const double per_cu = bytes / busy_cus / (kGBsPerCU * 1e3);
+    stream = stream > per_cu ? stream : per_cu;
     c.us = kUsLaunch + (stream > compute ? stream : compute) +
            (splits > 1 ? kUsHandoff + kUsPerSplit * splits : 0.0);
     return c;
