@@ -1370,6 +1370,13 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
             if (c.us < best.us * 0.98) best = c;
         }
     }
+    // A tall plan whose workgroups hold fewer groups than waves leaves waves idle; the wide
+    // shape with the same split count is then ~3% faster when the model scores them alike
+    // (measured on qkv and o at M = 5: 7.72 -> 7.48 us and 7.53 -> 7.30 us).
+    if (best.v == &kTall && (groups + best.splits - 1) / best.splits < kTall.waves) {
+        const Choice w = score(kWide, base, groups, best.splits, av, K, N, bits);
+        if (w.us <= best.us * 1.02) best = w;
+    }
     // Balanced wide plan.  When the plain wide plan wins and its tiles fill r whole rounds of
     // CUs (r workgroups on every CU) plus a remainder, the busiest CUs hold r + 1 whole
     // tiles.  Instead, r*256 tiles run unsplit (dispatched first, r per CU) and the remaining
