@@ -215,3 +215,19 @@ def test_plan_covers_shapes():
 def test_no_device_is_reported():
     # valid arguments on a host with no GPU: the device check fails before any launch
     assert _gemm(A16, W16, S8, Z4, C16, 5, 128, 64, None) == 4
+
+
+def test_measured_plan_choices():
+    # plan decisions backed by measured launches (graph replays, HBM-resident weights):
+    # qkv and o at M=5 take the wide shape at 3 splits (a tall workgroup would leave waves
+    # idle), down keeps the tall shape at 4 splits, and 8-bit down at M=1 spreads over 96 CUs
+    for K, N in ((3584, 4608), (3584, 3584)):
+        p = w4.plan(5, K, N)
+        assert (p["kernel"], p["splits"]) == (1, 3), (K, N, p)
+    p = w4.plan(5, 18944, 3584)
+    assert (p["kernel"], p["splits"]) == (2, 4), p
+    p = w4.plan(1, 8960, 1536, bits=8)
+    assert (p["kernel"], p["splits"], p["workgroups"]) == (5, 4, 96), p
+    # gate_up at M=5: two whole rounds unsplit, the remaining 80 tiles split three ways
+    p = w4.plan(5, 3584, 37888)
+    assert (p["kernel"], p["full_tiles"], p["splits"], p["workgroups"]) == (1, 512, 3, 752), p
