@@ -207,3 +207,22 @@ def test_workload_w4a4_draft_sampled(orc):
         cols = np.unique(np.r_[0, spec.N - 1, r.integers(0, spec.N, 48)])
         Cr, Cabs = orc.gemm_a4(x.Aq, x.As, x.Wq, x.S, x.Z, cols=cols)
         check(C[:, cols], Cr, Cabs, spec.name)
+
+
+def test_maximum_size_a4(orc):
+    # activation codes just under 2 GiB (M * K / 2 bytes), the largest array the kernel's
+    # 32-bit byte offsets address; sampled rows (edges, row-block boundaries) and all columns
+    M, K, N = 32767, 131072, 8
+    assert M * K // 2 < 1 << 31
+    p = w4.plan(M, K, N, a4=True)
+    log(f"w4a4 maximum size M={M} K={K} N={N} plan={p}")
+    x = synth.generate_custom(1, K, N, seed=31)  # weights; activations drawn below
+    r = np.random.default_rng(32)
+    Aq = r.integers(0, 1 << 32, size=(M, K // 8), dtype=np.uint32)
+    As = ((2.5 + 0.3 * np.abs(r.standard_normal((M, K // 128)))) / 7.0).astype(np.float32)
+    Aq_d, As_d = dev_a4(Aq, As)
+    C = run_a4(Aq_d, As_d, to_dev(x)).cpu().numpy()
+    del Aq_d, As_d
+    rows = np.unique(np.r_[0, 15, 16, M - 17, M - 16, M - 1, r.integers(0, M, 6)]).astype(np.int64)
+    Cr, Cabs = orc.gemm_a4(Aq[rows], As[rows], x.Wq, x.S, x.Z)
+    check(C[rows], Cr, Cabs, f"w4a4 max size M={M} K={K} N={N}")
