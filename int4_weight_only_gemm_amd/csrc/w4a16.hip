@@ -74,6 +74,10 @@ struct Variant {
 constexpr Variant kWide = {4, 3};
 constexpr Variant kTall = {12, 1};
 constexpr int kOccupancy = 3;  // waves per SIMD: at most 168 VGPRs per lane
+// 32-row blocks (two row tiles per wave) need more registers: 2 waves per SIMD.
+constexpr Variant kWide2 = {4, 2};
+constexpr Variant kTall2 = {8, 1};
+constexpr int kOccupancy2 = 2;  // at most 256 VGPRs per lane
 
 struct SmallParams {
     const uint16_t *A;  // bfloat16 [M, K]; with 4-bit activations the packed codes [M, K/8]
@@ -304,8 +308,10 @@ struct PipeRegs {
     typename std::conditional<A4, u32x2, u32x4>::type a[AV];
 };
 
-constexpr int kPipeWaveBytes = kTileM * kARowBytes + kTileM * 4;  // tile + row exponents
-constexpr int kPipeExpOffset = kTileM * kARowBytes;
+// Per-wave LDS: the activation tile (RB row tiles of 16 rows) and one word per row (the
+// power-of-two exponent, or the 4-bit activations' scale).
+constexpr int pipe_wave_bytes(int rb) { return rb * (kTileM * kARowBytes + kTileM * 4); }
+constexpr int pipe_exp_offset(int rb) { return rb * kTileM * kARowBytes; }
 
 template <bool VEC, int AV, int BITS, bool A4>
 __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources &rs, const LaneOffsets<VEC> &o,
@@ -336,9 +342,10 @@ __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources 
 // the tile.  The 16 chunks of a row sit in 16 consecutive lanes.  4-bit activations are
 // unpacked instead (offset-binary codes, zero point 8, exact in binary16, in the weight
 // operand's element order) and the row's float32 scale is stored in place of x[r].
-template <int AV, int BITS, bool A4>
+template <int AV, int BITS, bool A4, int RB>
 __device__ __forceinline__ void stage_pipe(const PipeRegs<AV, BITS, A4> &r, char *lds_wave, int mv, int lane)
 {
+    constexpr int kExpOffset = pipe_exp_offset(RB);
     asm volatile("" ::: "memory");  // the previous group's LDS reads stay before these writes
     const int kc = lane & 15;
     if constexpr (A4) {
@@ -350,7 +357,7 @@ __device__ __forceinline__ void stage_pipe(const PipeRegs<AV, BITS, A4> &r, char
             const int row = 4 * i + (lane >> 4);
             const f16x8 v = unpack8(r.a[i].x, zlo, zhi, magic);
             if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = __builtin_bit_cast(u32x4, v);
-            if (kc == 0) *(uint32_t *)(lds_wave + kPipeExpOffset + 4 * row) = row < mv ? r.a[i].y : 0u;
+            if (kc == 0) *(uint32_t *)(lds_wave + kExpOffset + 4 * row) = row < mv ? r.a[i].y : 0u;
         }
     } else {
 #pragma unroll
@@ -359,18 +366,21 @@ __device__ __forceinline__ void stage_pipe(const PipeRegs<AV, BITS, A4> &r, char
             const int e = row16_max(chunk_max_exp(r.a[i]));
             const int x = 142 - max(e, 1);
             if (row < mv) *(u32x4 *)(lds_wave + row * kARowBytes + kc * 16) = convert_chunk<BITS>(r.a[i], x);
-            if (kc == 0) *(int *)(lds_wave + kPipeExpOffset + 4 * row) = row < mv ? x : 0;
+            if (kc == 0) *(int *)(lds_wave + kExpOffset + 4 * row) = row < mv ? x : 0;
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's tile is complete
 }
 
-template <int AV, int BITS, bool A4>
+template <int AV, int BITS, bool A4, int RB>
 __device__ __forceinline__ void compute_pipe(const PipeRegs<AV, BITS, A4> &r, const char *lds_wave, int mv, int lane,
-                                             f32x4 (&acc)[4])
+                                             f32x4 (&acc)[RB][4])
 {
+    constexpr int kExpOffset = pipe_exp_offset(RB);
     const int c = lane & 15, kq = lane >> 4;
-    f32x4 P[4];
+    // row tile rb of the block holds rows 16 rb .. 16 rb + 15; each unpacked weight operand
+    // feeds the matrix-core step of every row tile
+    f32x4 P[RB][4];
     if constexpr (BITS == 4) {
         uint32_t magic;
         asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
@@ -384,14 +394,21 @@ __device__ __forceinline__ void compute_pipe(const PipeRegs<AV, BITS, A4> &r, co
         }
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            // rows mv..15 of the tile are zero (cleared once, never staged)
-            const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_wave + c * kARowBytes + (4 * st + kq) * 16));
+            // rows mv.. of the tile are zero (cleared once, never staged)
+            f16x8 a_op[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                a_op[rb] = __builtin_bit_cast(
+                    f16x8, *(const u32x4 *)(lds_wave + (16 * rb + c) * kARowBytes + (4 * st + kq) * 16));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const f16x8 b_op = unpack8(r.w[st][t], zlo[t], zhi[t], magic);
-                // the first k-step starts from a literal zero accumulator (no register clearing)
-                const f32x4 c_in = st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[t];
-                P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, c_in, 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    // the first k-step starts from a literal zero accumulator (no register clearing)
+                    const f32x4 c_in = st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[rb][t];
+                    P[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op[rb], b_op, c_in, 0, 0, 0);
+                }
             }
         }
     } else {
@@ -408,43 +425,59 @@ __device__ __forceinline__ void compute_pipe(const PipeRegs<AV, BITS, A4> &r, co
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds_wave + c * kARowBytes + (4 * ks + kq) * 16));
+            f16x8 a_op[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                a_op[rb] = __builtin_bit_cast(
+                    f16x8, *(const u32x4 *)(lds_wave + (16 * rb + c) * kARowBytes + (4 * ks + kq) * 16));
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const f16x8 b_op = unpack8_w8(r.w[2 * ks][t], r.w[2 * ks + 1][t], zneg[t], magic, sel01, sel23);
-                const f32x4 c_in = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[t];
-                P[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, c_in, 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const f32x4 c_in = ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P[rb][t];
+                    P[rb][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op[rb], b_op, c_in, 0, 0, 0);
+                }
             }
         }
     }
     if constexpr (A4) {
         // the group's partials are exact integers; each is scaled by its row's activation
         // scale times its column's weight scale
-        const f32x4 sa = *(const f32x4 *)(lds_wave + kPipeExpOffset + 16 * kq);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
-            const float sv = (float)__builtin_bit_cast(_Float16, sb);
+        for (int rb = 0; rb < RB; ++rb) {
+            const f32x4 sa = *(const f32x4 *)(lds_wave + kExpOffset + 64 * rb + 16 * kq);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(sv * sa[i], P[t][i], acc[t][i]);
+            for (int t = 0; t < 4; ++t) {
+                const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
+                const float sv = (float)__builtin_bit_cast(_Float16, sb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[rb][t][i] = __builtin_fmaf(sv * sa[i], P[rb][t][i], acc[rb][t][i]);
+            }
         }
     } else {
-        const int4 xr = *(const int4 *)(lds_wave + kPipeExpOffset + 16 * kq);
-        const int xs[4] = {xr.x, xr.y, xr.z, xr.w};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
-            const float sv = (float)__builtin_bit_cast(_Float16, sb);
+        for (int rb = 0; rb < RB; ++rb) {
+            const int4 xr = *(const int4 *)(lds_wave + kExpOffset + 64 * rb + 16 * kq);
+            const int xs[4] = {xr.x, xr.y, xr.z, xr.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(ldexpf(sv, -xs[i]), P[t][i], acc[t][i]);
+            for (int t = 0; t < 4; ++t) {
+                const uint16_t sb = (uint16_t)(r.s[t >> 1] >> (16 * (t & 1)));
+                const float sv = (float)__builtin_bit_cast(_Float16, sb);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[rb][t][i] = __builtin_fmaf(ldexpf(sv, -xs[i]), P[rb][t][i], acc[rb][t][i]);
+            }
         }
     }
 }
 
-template <bool VEC, int WAVES, int AV, int OCC, int BITS, bool A4>
+template <bool VEC, int WAVES, int AV, int OCC, int BITS, bool A4, int RB>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void w4a16_kernel(SmallParams p)
 {
+    constexpr int kRows = RB * kTileM;  // rows per block: one or two matrix-core row tiles
+    constexpr int kExpOffset = pipe_exp_offset(RB);
     extern __shared__ __attribute__((aligned(16))) char lds[];  // per-wave tiles, then reduction
     __shared__ int s_last;
 
@@ -469,8 +502,8 @@ void w4a16_kernel(SmallParams p)
     // XCD and the second block's weight loads find the lines the first one brought in.
     const int mb = (int)(tile % (uint32_t)p.m_blocks);
     const int nt = (int)(tile / (uint32_t)p.m_blocks);
-    const int n0 = nt * kTileN, m0 = mb * kTileM;
-    const int mv = (p.M - m0 < kTileM) ? (int)(p.M - m0) : kTileM;
+    const int n0 = nt * kTileN, m0 = mb * kRows;
+    const int mv = (p.M - m0 < kRows) ? (int)(p.M - m0) : kRows;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
     const int c = lane & 15, kq = lane >> 4;
@@ -479,7 +512,7 @@ void w4a16_kernel(SmallParams p)
     const int g_end = min(p.groups, g_begin + gps);
     const int g0 = g_begin + wave;
     const int n_my = g0 < g_end ? (g_end - g0 + WAVES - 1) / WAVES : 0;
-    char *tile_lds = lds + wave * kPipeWaveBytes;
+    char *tile_lds = lds + wave * pipe_wave_bytes(RB);
 
     Resources rs;
     rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K * BITS / 32 * p.N * 4), kRsrcWord3);
@@ -503,22 +536,24 @@ void w4a16_kernel(SmallParams p)
             asoff[i] = 0;
         }
     }
-    // rows 4*AV..15 of this wave's exponent table are never staged: they read as 0; rows
-    // mv..15 of its activation tile are never staged either: they read as 0 in the MFMAs
-    if (4 * AV < kTileM && lane >= 4 * AV && lane < kTileM) *(int *)(tile_lds + kPipeExpOffset + 4 * lane) = 0;
-    for (int i = lane; i < (kTileM - mv) * (kARowBytes / 16); i += kWave)
+    // rows 4*AV.. of this wave's exponent table are never staged: they read as 0; rows mv..
+    // of its activation tile are never staged either: they read as 0 in the MFMAs
+    if (4 * AV < kRows && lane >= 4 * AV && lane < kRows) *(int *)(tile_lds + kExpOffset + 4 * lane) = 0;
+    for (int i = lane; i < (kRows - mv) * (kARowBytes / 16); i += kWave)
         *(u32x4 *)(tile_lds + mv * kARowBytes + i * 16) = u32x4{0u, 0u, 0u, 0u};
 
-    f32x4 acc[4];
+    f32x4 acc[RB][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Two register slots: group j+1 (weights and activations) is in flight while group j is
     // converted and computed.
     auto G = [&](int j) { return g0 + WAVES * j; };
     auto run = [&](const PipeRegs<AV, BITS, A4> &r) {
-        stage_pipe<AV, BITS, A4>(r, tile_lds, mv, lane);
-        compute_pipe<AV, BITS, A4>(r, tile_lds, mv, lane, acc);
+        stage_pipe<AV, BITS, A4, RB>(r, tile_lds, mv, lane);
+        compute_pipe<AV, BITS, A4, RB>(r, tile_lds, mv, lane, acc);
     };
     if (n_my > 0) {
         PipeRegs<AV, BITS, A4> r0, r1;
@@ -543,24 +578,34 @@ void w4a16_kernel(SmallParams p)
     __syncthreads();
     float *red = (float *)lds;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 4 * kq + i;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * rb + 4 * kq + i;
+            if (row < mv) {
+                f32x4 v = {acc[rb][0][i], acc[rb][1][i], acc[rb][2][i], acc[rb][3][i]};
+                *(f32x4 *)(red + (wave * mv + row) * kTileN + 4 * c) = v;
+            }
+        }
+    __syncthreads();
+    // Each thread owns one 4-column quad of up to kPasses rows: 16 threads per row, so a
+    // workgroup covers WAVES * 4 rows per pass.
+    constexpr int kRowsPerPass = WAVES * 4;
+    constexpr int kPasses = (kRows + kRowsPerPass - 1) / kRowsPerPass;
+    const int row0 = threadIdx.x >> 4, quad = threadIdx.x & 15;
+    f32x4 sum[kPasses];
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+        const int row = row0 + ps * kRowsPerPass;
+        sum[ps] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (row < mv) {
-            f32x4 v = {acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
-            *(f32x4 *)(red + (wave * mv + row) * kTileN + 4 * c) = v;
+            sum[ps] = *(const f32x4 *)(red + row * kTileN + 4 * quad);
+#pragma unroll
+            for (int w = 1; w < WAVES; ++w) sum[ps] += *(const f32x4 *)(red + (w * mv + row) * kTileN + 4 * quad);
         }
     }
-    __syncthreads();
-    const int row = threadIdx.x >> 4, quad = threadIdx.x & 15;
-    const bool valid = row < mv;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-        sum = *(const f32x4 *)(red + row * kTileN + 4 * quad);
-#pragma unroll
-        for (int w = 1; w < WAVES; ++w) sum += *(const f32x4 *)(red + (w * mv + row) * kTileN + 4 * quad);
-    }
     const int64_t col = n0 + 4 * quad;
-    auto store_c = [&](const f32x4 &v) {
+    auto store_c = [&](int row, const f32x4 &v) {
         float *dst = p.C + (int64_t)(m0 + row) * p.N + col;
         if (VEC) {
             if (col < p.N) *(f32x4 *)dst = v;
@@ -571,20 +616,27 @@ void w4a16_kernel(SmallParams p)
         }
     };
     if (!split) {
-        if (valid) store_c(sum);
+#pragma unroll
+        for (int ps = 0; ps < kPasses; ++ps)
+            if (row0 + ps * kRowsPerPass < mv) store_c(row0 + ps * kRowsPerPass, sum[ps]);
         return;
     }
     // Partials travel as 16-byte device-coherent stores and loads (the cache policy of
-    // agent-scope atomics), one per lane and split.
+    // agent-scope atomics), one per lane, pass and split.
     const uint32_t stile = tile - nfull;  // index among the split tiles
     const int64_t split_tiles = (int64_t)p.m_blocks * p.n_tiles - nfull;
+    constexpr uint32_t kPartBytes = kRows * kTileN * 4;  // one split's partial tile
     const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)p.part, (short)0, (int)(split_tiles * p.splits * (kTileM * kTileN * 4)), kRsrcWord3);
-    constexpr uint32_t kPartBytes = kTileM * kTileN * 4;  // one split's partial tile
-    const uint32_t lane_part = (uint32_t)stile * (uint32_t)p.splits * kPartBytes + (uint32_t)(row * kTileN + 4 * quad) * 4;
-    if (valid)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sum), prs, lane_part + (uint32_t)sp * kPartBytes,
-                                               0, kCacheCoherent);
+        (void *)p.part, (short)0, (int)(split_tiles * p.splits * kPartBytes), kRsrcWord3);
+    const uint32_t tile_part = (uint32_t)stile * (uint32_t)p.splits * kPartBytes;
+    auto lane_part = [&](int row) { return tile_part + (uint32_t)(row * kTileN + 4 * quad) * 4; };
+#pragma unroll
+    for (int ps = 0; ps < kPasses; ++ps) {
+        const int row = row0 + ps * kRowsPerPass;
+        if (row < mv)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sum[ps]), prs,
+                                                   lane_part(row) + (uint32_t)sp * kPartBytes, 0, kCacheCoherent);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -594,22 +646,27 @@ void w4a16_kernel(SmallParams p)
     __syncthreads();
     if (!s_last) return;
     asm volatile("" ::: "memory");
-    if (valid) {
-        // up to kBatch splits' partials in flight at once, summed in split order
-        constexpr int kBatch = 8;
-        f32x4 tot = {0.f, 0.f, 0.f, 0.f};
-        for (int b = 0; b < p.splits; b += kBatch) {
-            u32x4 v[kBatch];
 #pragma unroll
-            for (int i = 0; i < kBatch; ++i) {
-                const int s2 = b + i < p.splits ? b + i : p.splits - 1;  // clamped: no branch around loads
-                v[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, lane_part + (uint32_t)s2 * kPartBytes, 0, kCacheCoherent);
+    for (int ps = 0; ps < kPasses; ++ps) {
+        const int row = row0 + ps * kRowsPerPass;
+        if (row < mv) {
+            // up to kBatch splits' partials in flight at once, summed in split order
+            constexpr int kBatch = 8;
+            f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+            for (int b = 0; b < p.splits; b += kBatch) {
+                u32x4 v[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i) {
+                    const int s2 = b + i < p.splits ? b + i : p.splits - 1;  // clamped: no branch around loads
+                    v[i] = __builtin_amdgcn_raw_buffer_load_b128(prs, lane_part(row) + (uint32_t)s2 * kPartBytes, 0,
+                                                                 kCacheCoherent);
+                }
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    if (b + i < p.splits) tot += __builtin_bit_cast(f32x4, v[i]);
             }
-#pragma unroll
-            for (int i = 0; i < kBatch; ++i)
-                if (b + i < p.splits) tot += __builtin_bit_cast(f32x4, v[i]);
+            store_c(row, tot);
         }
-        store_c(tot);
     }
     if (threadIdx.x == 0) __hip_atomic_store(p.count + stile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1358,11 +1415,20 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
 {
     const int groups = (int)(K / kGroup);
     const int n_tiles = (int)((N + kTileN - 1) / kTileN);
-    const int m_blocks = (int)((M + kTileM - 1) / kTileM);
+    // Blocks of 16 rows.  With 4-bit activations at 17 to 32 rows, one block of 32: each wave
+    // holds two matrix-core row tiles that share every unpacked weight operand (the
+    // Llama-2-7B batch-32 draft step measured 1.94 -> 1.78 ms).  Not for bfloat16
+    // activations, whose per-wave conversion doubles with the rows: there the same change
+    // measured between 7% faster and 31% slower by shape, and beyond 32 rows a second block
+    // mostly computes padding.
+    const int rows = a4 && M > kTileM && M <= 2 * kTileM ? 2 * kTileM : kTileM;
+    const int m_blocks = (int)((M + rows - 1) / rows);
     const int64_t base = (int64_t)n_tiles * m_blocks;
     Choice best = {&kWide, 1, 1e30};  // fallback (more tiles than resident slots): wide, no split
-    const int av = (int)(((M < kTileM ? M : kTileM) + 3) / 4);
-    for (const Variant *v : {&kTall, &kWide}) {  // tall first: it keeps near-ties
+    const int av = (int)(((M < rows ? M : rows) + 3) / 4);
+    const Variant &wide = rows > kTileM ? kWide2 : kWide, &tall = rows > kTileM ? kTall2 : kTall;
+    best.v = &wide;
+    for (const Variant *v : {&tall, &wide}) {  // tall first: it keeps near-ties
         for (int sp = 1; sp <= groups; ++sp) {
             const int gps = (groups + sp - 1) / sp;
             if ((groups + gps - 1) / gps != sp) continue;
@@ -1373,8 +1439,8 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     // A tall plan whose workgroups hold fewer groups than waves leaves waves idle; the wide
     // shape with the same split count is then ~3% faster when the model scores them alike
     // (measured on qkv and o at M = 5: 7.72 -> 7.48 us and 7.53 -> 7.30 us).
-    if (best.v == &kTall && (groups + best.splits - 1) / best.splits < kTall.waves) {
-        const Choice w = score(kWide, base, groups, best.splits, av, K, N, bits);
+    if (best.v == &tall && (groups + best.splits - 1) / best.splits < tall.waves) {
+        const Choice w = score(wide, base, groups, best.splits, av, K, N, bits);
         if (w.us <= best.us * 1.02) best = w;
     }
     // Balanced wide plan.  When the plain wide plan wins and its tiles fill r whole rounds of
@@ -1386,9 +1452,9 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     // extra launch width cost more than the balance gains (measured).
     int64_t full = 0;
     const int r = (int)(base / kCUs);
-    if (best.v == &kWide && best.splits == 1 && r >= 1 && r < kWide.per_cu && base % kCUs != 0) {
+    if (best.v == &wide && best.splits == 1 && r >= 1 && r < wide.per_cu && base % kCUs != 0) {
         const int64_t rem = base - (int64_t)r * kCUs;
-        int64_t sp = (int64_t)kCUs * (kWide.per_cu - r) / rem;
+        int64_t sp = (int64_t)kCUs * (wide.per_cu - r) / rem;
         sp = sp < groups / kMinPartGroups ? sp : groups / kMinPartGroups;
         if (sp >= 2) {
             const int g = (int)((groups + sp - 1) / sp);
@@ -1399,8 +1465,8 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     const int gps = (groups + best.splits - 1) / best.splits;
     const int splits = (groups + gps - 1) / gps;
     const int64_t split_tiles = splits > 1 ? base - full : 0;
-    pl->kernel = small_kernel_id(best.v == &kTall, bits, a4);
-    pl->tile_m = kTileM;
+    pl->kernel = small_kernel_id(best.v == &tall, bits, a4);
+    pl->tile_m = rows;
     pl->tile_n = kTileN;
     pl->m_blocks = m_blocks;
     pl->n_tiles = n_tiles;
@@ -1408,7 +1474,7 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     pl->groups_per_split = gps;
     pl->full_tiles = (int)full;
     pl->workgroups = full + (base - full) * splits;
-    pl->workspace_bytes = split_tiles * 4 + split_tiles * splits * kTileM * kTileN * 4;
+    pl->workspace_bytes = split_tiles * 4 + split_tiles * splits * rows * kTileN * 4;
 }
 
 // Shapes chosen by large_path run on the bf16 matrix-core kernel; everything else on the
@@ -1423,25 +1489,36 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 
 size_t plan_lds_bytes(int64_t M, const w4_plan &pl)
 {
-    const int rows = M < kTileM ? (int)M : kTileM;
-    const Variant &v = (pl.kernel == 2 || pl.kernel == 5 || pl.kernel == 7) ? kTall : kWide;
-    const size_t tiles = (size_t)v.waves * kPipeWaveBytes;
+    const int rows = M < pl.tile_m ? (int)M : pl.tile_m;
+    const bool tall = pl.kernel == 2 || pl.kernel == 5 || pl.kernel == 7;
+    const Variant &v = pl.tile_m > kTileM ? (tall ? kTall2 : kWide2) : (tall ? kTall : kWide);
+    const size_t tiles = (size_t)v.waves * pipe_wave_bytes(pl.tile_m / kTileM);
     const size_t red = (size_t)v.waves * rows * kTileN * 4;
     return tiles > red ? tiles : red;
 }
 
 // Small-M launches: one instantiation per (vectorized loads, waves, activation chunks per
 // lane, code width); every shape keeps 3 waves per SIMD.
-template <int BITS, int WAVES, bool A4>
-void launch_small(int av, bool vec, dim3 grid, size_t lds, hipStream_t s, const SmallParams &p)
+template <int BITS, bool A4>
+void launch_small(bool tall, int rb, int av, bool vec, dim3 grid, size_t lds, hipStream_t s, const SmallParams &p)
 {
-#define W4_LAUNCH(V, AVV) \
-    hipLaunchKernelGGL((w4a16_kernel<V, WAVES, AVV, kOccupancy, BITS, A4>), grid, dim3(WAVES * kWave), lds, s, p)
-#define W4_LAUNCH_AV(V) \
-    switch (av) { case 1: W4_LAUNCH(V, 1); break; case 2: W4_LAUNCH(V, 2); break; \
-                  case 3: W4_LAUNCH(V, 3); break; default: W4_LAUNCH(V, 4); break; }
-    if (vec) { W4_LAUNCH_AV(true) } else { W4_LAUNCH_AV(false) }
-#undef W4_LAUNCH_AV
+#define W4_LAUNCH(V, WV, AVV, OCCV, RBV) \
+    hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, OCCV, BITS, A4, RBV>), grid, dim3(WV * kWave), lds, s, p)
+#define W4_LAUNCH_16(V, WV) \
+    switch (av) { case 1: W4_LAUNCH(V, WV, 1, kOccupancy, 1); break; case 2: W4_LAUNCH(V, WV, 2, kOccupancy, 1); break; \
+                  case 3: W4_LAUNCH(V, WV, 3, kOccupancy, 1); break; default: W4_LAUNCH(V, WV, 4, kOccupancy, 1); break; }
+#define W4_LAUNCH_32(V, WV) \
+    switch (av) { case 5: W4_LAUNCH(V, WV, 5, kOccupancy2, 2); break; case 6: W4_LAUNCH(V, WV, 6, kOccupancy2, 2); break; \
+                  case 7: W4_LAUNCH(V, WV, 7, kOccupancy2, 2); break; default: W4_LAUNCH(V, WV, 8, kOccupancy2, 2); break; }
+    if (rb == 1) {
+        if (tall) { if (vec) { W4_LAUNCH_16(true, kTall.waves) } else { W4_LAUNCH_16(false, kTall.waves) } }
+        else { if (vec) { W4_LAUNCH_16(true, kWide.waves) } else { W4_LAUNCH_16(false, kWide.waves) } }
+    } else if constexpr (A4) {  // 32-row blocks are planned for 4-bit activations only
+        if (tall) { if (vec) { W4_LAUNCH_32(true, kTall2.waves) } else { W4_LAUNCH_32(false, kTall2.waves) } }
+        else { if (vec) { W4_LAUNCH_32(true, kWide2.waves) } else { W4_LAUNCH_32(false, kWide2.waves) } }
+    }
+#undef W4_LAUNCH_32
+#undef W4_LAUNCH_16
 #undef W4_LAUNCH
 }
 
@@ -1542,19 +1619,16 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         p.full_tiles = pl.full_tiles;
         const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros, 4);
         const size_t lds = plan_lds_bytes(M, pl);
-        const int rows = M < kTileM ? (int)M : kTileM;
+        const int rb = pl.tile_m / kTileM;
+        const int rows = M < pl.tile_m ? (int)M : pl.tile_m;
         const int av = (rows + 3) / 4;
         const bool tall = pl.kernel == 2 || pl.kernel == 5 || pl.kernel == 7;
-        if (a4) {
-            if (tall) launch_small<4, kTall.waves, true>(av, vec, grid, lds, s, p);
-            else launch_small<4, kWide.waves, true>(av, vec, grid, lds, s, p);
-        } else if (bits == 8) {
-            if (tall) launch_small<8, kTall.waves, false>(av, vec, grid, lds, s, p);
-            else launch_small<8, kWide.waves, false>(av, vec, grid, lds, s, p);
-        } else {
-            if (tall) launch_small<4, kTall.waves, false>(av, vec, grid, lds, s, p);
-            else launch_small<4, kWide.waves, false>(av, vec, grid, lds, s, p);
-        }
+        if (a4)
+            launch_small<4, true>(tall, rb, av, vec, grid, lds, s, p);
+        else if (bits == 8)
+            launch_small<8, false>(tall, rb, av, vec, grid, lds, s, p);
+        else
+            launch_small<4, false>(tall, rb, av, vec, grid, lds, s, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(name, e);

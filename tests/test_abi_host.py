@@ -193,8 +193,8 @@ def test_plan_covers_shapes():
         if True:
             if p["kernel"] == 3:
                 assert p["tile_n"] == 256 and p["tile_m"] <= 160
-            else:
-                assert (p["tile_m"], p["tile_n"]) == (16, 64)
+            else:  # 16-row blocks, or (4-bit activations) one 32-row block at 17..32 rows
+                assert (p["tile_m"], p["tile_n"]) == ((32 if a4 and 16 < M <= 32 else 16), 64)
             assert p["n_tiles"] * p["tile_n"] >= N > (p["n_tiles"] - 1) * p["tile_n"]
             assert p["m_blocks"] * p["tile_m"] >= M > (p["m_blocks"] - 1) * p["tile_m"]
             assert p["splits"] * p["groups_per_split"] >= groups
@@ -206,7 +206,8 @@ def test_plan_covers_shapes():
             assert p["workgroups"] == full + (tiles - full) * p["splits"]
             assert (p["workspace_bytes"] > 0) == (p["splits"] > 1)
             if p["kernel"] != 3:  # every workgroup resident at once
-                assert p["workgroups"] <= 256 * (3 if p["kernel"] in (1, 4, 6) else 1) or p["splits"] == 1
+                per_cu = (2 if p["tile_m"] == 32 else 3) if p["kernel"] in (1, 4, 6) else 1
+                assert p["workgroups"] <= 256 * per_cu or p["splits"] == 1
     with pytest.raises(w4.W4Error):
         w4.plan(5, 100, 64)
 

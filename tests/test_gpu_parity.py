@@ -176,7 +176,8 @@ def test_split_k_shapes(orc, M, K, N):
     check(C[:, cols], Cr, Cabs, f"split M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("M,K,N", [(5, 1024, 19200), (20, 1024, 9600), (3, 2048, 19198), (1, 3584, 37888)])
+@pytest.mark.parametrize("M,K,N", [(5, 1024, 19200), (20, 1024, 16640), (40, 2048, 8576), (3, 2048, 19198),
+                                   (1, 3584, 37888)])
 def test_balanced_wide_plan(orc, M, K, N):
     # whole rounds of unsplit tiles plus split remainder tiles: both kinds of workgroup, the
     # split tiles' counters and partials, row blocks crossing the boundary, ragged N
@@ -193,9 +194,11 @@ def test_balanced_wide_plan(orc, M, K, N):
     if M * K * N <= 400_000_000:
         cols = None
         Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
-    else:  # full-size shape: both column ranges, every split boundary's neighbourhood
-        cols = np.unique(np.r_[0, 64 * p["full_tiles"] - 1, 64 * p["full_tiles"], N - 1,
-                               np.random.default_rng(22).integers(0, N, 96)])
+    else:  # full-size shape: both column ranges, the neighbourhood of their boundary
+        # tile t covers row block t % m_blocks of column tile t / m_blocks
+        edge = 64 * (p["full_tiles"] // p["m_blocks"])
+        cols = np.unique(np.r_[0, edge - 1, edge, N - 1, np.random.default_rng(22).integers(0, N, 96)])
+        cols = cols[(cols >= 0) & (cols < N)]
         Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
         C = C[:, cols]
     check(C, Cr, Cabs, f"balanced M={M} K={K} N={N}")
