@@ -46,9 +46,15 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(path: str = KERNEL_SOURCE) -> str:
+    """Hash of the kernel source's code: comments, trailing spaces and blank lines removed,
+    so that a comment-only edit keeps the counters taken on that code valid."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def read_traffic(workload: str):

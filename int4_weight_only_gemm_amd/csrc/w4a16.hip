@@ -21,8 +21,12 @@
 //    own LDS tile, row r scaled by 2^x[r] so that the row's largest magnitude in the group
 //    lands in [2^15, 2^16); the scale is undone exactly when the group's float32 partial
 //    is rescaled by s.  Every product a*(q-z) is then exact; bfloat16 values more than
-//    2^29 below the largest magnitude of their row within the group may be flushed (error
-//    below 2^-29 of that maximum per element).
+//    2^33 below the largest magnitude of their row within the group are rounded to the
+//    binary16 subnormal grid (absolute error below 2^-40 of that maximum per element).
+//  * The same kernel, by template parameter, runs 8-bit codes (4 per word, full-byte zero
+//    points) and 4-bit activations (offset-binary codes with a float32 scale per row and
+//    group, unpacked like the weights), and holds one or two 16-row matrix-core tiles per
+//    wave (two share every unpacked weight operand).
 //  * Split-K across workgroups writes float32 partials to a workspace with device-coherent
 //    stores; a per-tile arrival counter elects the last workgroup, which sums the partials
 //    in split order, writes C and resets the counter.  One launch per GEMM, no memset, no
