@@ -118,7 +118,8 @@ def test_balanced_plan_a4(orc):
     check(C1.cpu().numpy(), Cr, Cabs, "w4a4 balanced")
 
 
-@pytest.mark.parametrize("M,K,N", [(5, 384, 72), (16, 1152, 64), (1, 4096, 33), (40, 256, 130)])
+@pytest.mark.parametrize("M,K,N", [(5, 384, 72), (16, 1152, 64), (1, 4096, 33), (40, 256, 130), (24, 384, 72),
+                                   (32, 1152, 130)])
 def test_one_hot_correctly_rounded_a4(orc, M, K, N):
     x = gen_a4(M, K, N, seed=4)
     dev = to_dev(x)
