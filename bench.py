@@ -99,8 +99,9 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the GEMM would shard by output columns; see DESIGN.md). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path (each GPU would "
+              "hold a column shard of every weight matrix and compute its columns of C). "
+              "Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
