@@ -232,3 +232,15 @@ def test_measured_plan_choices():
     # gate_up at M=5: two whole rounds unsplit, the remaining 80 tiles split three ways
     p = w4.plan(5, 3584, 37888)
     assert (p["kernel"], p["full_tiles"], p["splits"], p["workgroups"]) == (1, 512, 3, 752), p
+    # bf16 kernel at M = 64..96: splits of at least 4 groups, with two row blocks (qkv and o
+    # at M=64: 1 x 14 splits measured 20.6 and 18.6 us, 2 x 7 measured 16.8 and 15.3 us);
+    # the M=160 plans are the model's (within 3% of the fastest forced plan per shape)
+    for M, K, N, want in ((64, 3584, 4608, (2, 32, 7)), (64, 3584, 3584, (2, 32, 7)), (96, 3584, 3584, (2, 48, 7)),
+                          (64, 4096, 4096, (2, 32, 8)), (160, 4096, 12288, (1, 160, 5)),
+                          (160, 4096, 4096, (2, 80, 8)), (160, 4096, 22016, (1, 160, 2)),
+                          (160, 11008, 4096, (1, 160, 15))):
+        p = w4.plan(M, K, N)
+        assert p["kernel"] == 3 and (p["m_blocks"], p["tile_m"], p["splits"]) == want, (M, K, N, p)
+    # where splits of 4 groups would leave most CUs idle, the model's plan stands
+    p = w4.plan(64, 2048, 2048)
+    assert (p["m_blocks"], p["splits"], p["groups_per_split"]) == (1, 16, 1), p

@@ -512,7 +512,8 @@ def test_large_m_grid(orc, M):
 
 
 @pytest.mark.parametrize("M,K,N", [(160, 4096, 4096), (160, 11008, 4096), (64, 8192, 512), (200, 2048, 1030),
-                                   (160, 4096, 12288)])
+                                   (160, 4096, 12288), (64, 4096, 4096), (96, 3584, 3584), (64, 8960, 1536),
+                                   (80, 2048, 8192)])
 def test_large_m_split_k(orc, M, K, N):
     p = w4.plan(M, K, N)
     log(f"large split-K M={M} K={K} N={N} plan={p}")
