@@ -177,6 +177,10 @@ def test_plan_covers_shapes():
     shapes = [(g.M, g.K, g.N, g.bits, g.act4) for wl in synth.WORKLOADS.values() for g in wl.gemms]
     shapes += [(M, K, N, bits, a4) for M in (1, 5, 16, 17, 40, 64, 160) for K, N in ((3584, 4608), (18944, 3584), (128, 3))
                for bits, a4 in ((8, False), (4, True))]
+    # the large-M search at every row count 17..200 on shapes where its 4-group floor, the
+    # 32-row blocks up to 64 rows and the half-chip guard each decide some plans
+    shapes += [(M, K, N, 4, False) for M in range(17, 201) for K, N in ((4096, 4096), (8960, 1536), (2048, 8192),
+                                                                         (1536, 2048), (2048, 2048), (11008, 4096))]
     for key in shapes:
         if key in seen:
             continue
