@@ -513,7 +513,7 @@ def test_large_m_grid(orc, M):
 
 @pytest.mark.parametrize("M,K,N", [(160, 4096, 4096), (160, 11008, 4096), (64, 8192, 512), (200, 2048, 1030),
                                    (160, 4096, 12288), (64, 4096, 4096), (96, 3584, 3584), (64, 8960, 1536),
-                                   (80, 2048, 8192)])
+                                   (80, 2048, 8192), (64, 3584, 3590)])
 def test_large_m_split_k(orc, M, K, N):
     p = w4.plan(M, K, N)
     log(f"large split-K M={M} K={K} N={N} plan={p}")
@@ -613,7 +613,8 @@ def test_large_m_graph_and_reproducible():
             assert torch.equal(e, o), f"replay {rep} differs from eager"
 
 
-@pytest.mark.parametrize("M,K,N", [(65, 8192, 3), (97, 4096, 131), (161, 2048, 2049), (70, 8192, 1)])
+@pytest.mark.parametrize("M,K,N", [(65, 8192, 3), (97, 4096, 131), (161, 2048, 2049), (70, 8192, 1),
+                                   (93, 8960, 1539)])
 def test_large_m_split_odd_sizes(orc, M, K, N):
     # split-K plans whose M*N is not a multiple of 4 exercise the reduction's tail path
     p = w4.plan(M, K, N)
