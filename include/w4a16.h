@@ -181,8 +181,9 @@ typedef struct w4_plan {
                                    8 waves, bf16 MFMA),
                                4, 5 = 8-bit codes (w8a16_gemm), wide and tall as 1, 2,
                                6, 7 = 4-bit activations (w4a4_gemm), wide and tall          */
-    int tile_m;             /* output rows per row block (16 for kernels 1, 2, 4 to 7; 1 to
-                               160 for kernel 3, computed in row tiles of 32)                */
+    int tile_m;             /* output rows per row block: 16 for kernels 1, 2, 4, 5; 16 for
+                               kernels 6, 7, except 32 at 17..32 rows; 1 to 160 for kernel
+                               3, computed in row tiles of 32                                */
     int tile_n;             /* output columns per workgroup tile (64, or 256 for kernel 3)   */
     int m_blocks;           /* row blocks of tile_m                                          */
     int n_tiles;            /* column tiles of tile_n                                        */
