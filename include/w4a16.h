@@ -104,7 +104,7 @@ w4_status w8a16_gemm(const void *A_bf16, const uint32_t *Wq8, const void *scales
  *   workspace, stream and errors as for w4a16_gemm.  Each group's inner sum is an exact
  *   integer; it is scaled by sa * s in float32, so every element is within
  *   1e-4 * sum_k |sa qa (q - z) s| + 1e-6 of the exact value.  Every M runs on the binary16
- *   matrix cores in row blocks of 16.
+ *   matrix cores, in row blocks of 16; at 17..32 rows, in one block of 32 rows.
  */
 w4_status w4a4_gemm(const uint32_t *Aq, const float *A_scales, const uint32_t *Wq, const void *scales_f16,
                     const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N, void *stream);
