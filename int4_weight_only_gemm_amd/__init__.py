@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 import re
-from typing import Dict, List, Optional
+from typing import Dict, List
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libw4a16.so")
