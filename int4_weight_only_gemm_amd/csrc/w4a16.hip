@@ -1460,8 +1460,13 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     }
     // A tall plan whose workgroups hold fewer groups than waves leaves waves idle; the wide
     // shape with the same split count is then ~3% faster when the model scores them alike
-    // (measured on qkv and o at M = 5: 7.72 -> 7.48 us and 7.53 -> 7.30 us).
-    if (best.v == &tall && (groups + best.splits - 1) / best.splits < tall.waves) {
+    // (measured on qkv and o at M = 5: 7.72 -> 7.48 us and 7.53 -> 7.30 us).  With a single
+    // 16-row block the same holds at exactly one group per wave (Qwen2.5-1.5B draft at M=1:
+    // qkv, o, down 4.52 -> 4.49, 4.70 -> 4.57, 7.36 -> 7.16 us; 8-bit qkv and o 5.69 -> 5.36
+    // and 5.70 -> 5.35 us); with more rows per workgroup the tall shape keeps it (measured
+    // 1-3% faster on 16-row blocks at M = 24..60, 12-14% on 32-row blocks).
+    const int best_gps = (groups + best.splits - 1) / best.splits;
+    if (best.v == &tall && (best_gps < tall.waves || (best_gps == tall.waves && m_blocks == 1 && rows == kTileM))) {
         const Choice w = score(wide, base, groups, best.splits, av, K, N, bits);
         if (w.us <= best.us * 1.02) best = w;
     }
