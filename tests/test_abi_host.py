@@ -245,6 +245,17 @@ def test_measured_plan_choices():
                           (160, 11008, 4096, (1, 160, 15))):
         p = w4.plan(M, K, N)
         assert p["kernel"] == 3 and (p["m_blocks"], p["tile_m"], p["splits"]) == want, (M, K, N, p)
+    # a single 16-row block hands a tall plan at one group per wave to the wide shape (M=1
+    # draft: qkv 4.52 -> 4.49, o 4.70 -> 4.57, down 7.36 -> 7.16 us; 8-bit qkv 5.69 -> 5.36 us);
+    # more rows per workgroup keep the tall shape (W4A4 at M=32: 9.21 tall, 10.30 wide)
+    for K, N, want in ((1536, 2048, (1, 1)), (1536, 1536, (1, 1)), (8960, 1536, (1, 6))):
+        p = w4.plan(1, K, N)
+        assert (p["kernel"], p["splits"]) == want, (K, N, p)
+    for K, N in ((1536, 2048), (1536, 1536)):
+        assert w4.plan(1, K, N, bits=8)["kernel"] == 4
+    assert w4.plan(24, 1536, 2048)["kernel"] == 2
+    p = w4.plan(32, 4096, 4096, a4=True)
+    assert (p["kernel"], p["tile_m"], p["splits"]) == (7, 32, 4), p
     # where splits of 4 groups would leave most CUs idle, the model's plan stands
     p = w4.plan(64, 2048, 2048)
     assert (p["m_blocks"], p["splits"], p["groups_per_split"]) == (1, 16, 1), p
