@@ -253,6 +253,9 @@ def test_measured_plan_choices():
         assert (p["kernel"], p["splits"]) == want, (K, N, p)
     for K, N in ((1536, 2048), (1536, 1536)):
         assert w4.plan(1, K, N, bits=8)["kernel"] == 4
+    # 8-bit codes at M <= 4: near-ties go to the wide shape (down at M=1: 9.41 tall, 8.60 wide)
+    p = w4.plan(1, 8960, 1536, bits=8)
+    assert (p["kernel"], p["splits"]) == (4, 4), p
     assert w4.plan(24, 1536, 2048)["kernel"] == 2
     p = w4.plan(32, 4096, 4096, a4=True)
     assert (p["kernel"], p["tile_m"], p["splits"]) == (7, 32, 4), p
