@@ -5,14 +5,18 @@ One step = every linear layer of one forward of the named workload (default: the
 Qwen2.5-7B-shaped verify pass at M = gamma + 1 = 5: 28 layers x {qkv, o, gate_up, down} =
 112 GEMMs), with all inputs resident in HBM before timing starts.  The step is captured
 once into a HIP graph and replayed; W untimed replays, then K timed replays bracketed by
-synchronization, timed with HIP events on the launch stream.
+synchronization, timed with HIP events on the launch stream (one event between consecutive
+replays, so the line carries the mean over the timed region and each replay's median and
+minimum).
 
 Printed (one JSON line): effective weight GB/s (weight bytes = 4-bit codes + fp16 scales
 + u8 zeros per 128, i.e. 0.5234375 B per weight, divided by the step time), the fraction
 of the 8 TB/s HBM peak, the dominant kernel's roofline figures (its average launch duration
 over the timed region, HBM traffic per launch from counters when a matching summary exists),
-the oracle timed on the host cores on a bounded sample, and the achievable read ceiling: the
-library's streaming-read probe over the same byte counts, one launch per GEMM, in a graph.
+the oracle timed on the host cores on a bounded sample (thread count and CPU model), and the
+achievable read ceilings: the library's streaming-read probe over the same byte counts, one
+launch per GEMM, in a graph; the same probe as one launch over 1 GiB; and, per GEMM shape of
+the step, that shape's GEMMs alone against the probe over their bytes.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-ceiling]
 """
@@ -40,6 +44,76 @@ KERNEL_NAME_LARGE = "w4a16_mfma_kernel"  # M >= 64 (and large GEMMs from M = 17)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_w4a16_kernel_qwen2.5-7b-verify-m5.md")
 CPU_SAMPLE_SECONDS = 10.0
 PROBE_BLOCKS = 768  # streaming-read probe: three workgroups of 256 lanes per CU
+ONE_LAUNCH_PROBE_BYTES = 1 << 30
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def graph_ms(torch, fn, stream, reps):
+    """Capture fn into a HIP graph on stream and return the median replay time in ms."""
+    with torch.cuda.stream(stream):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    with torch.cuda.stream(stream):
+        g.replay()
+        evs[0].record(stream)
+        for i in range(reps):
+            g.replay()
+            evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(reps))
+    del g
+    return t[len(t) // 2]
+
+
+def per_shape_ceilings(args, gemms, calls, stream, sink, dev):
+    """For each distinct GEMM shape of the step: its GEMMs alone (every copy the step holds,
+    so the weights stream from HBM as in the step) and the streaming-read probe over the same
+    byte counts, one launch per GEMM, as graph replays."""
+    import torch
+    import int4_weight_only_gemm_amd as w4
+    handle = stream.cuda_stream
+    shapes = {}
+    for (spec, _), call in zip(gemms, calls):
+        shapes.setdefault((spec.M, spec.K, spec.N, spec.bits, spec.act4), []).append((spec, call))
+    out = []
+    for (M, K, N, bits, a4), items in shapes.items():
+        def gemm_fn():
+            for _, (fn, c) in items:
+                rc = fn(*c, handle)
+                if rc:
+                    raise w4.W4Error(rc, fn.__name__)
+        nbytes = (items[0][0].weight_bytes + 15) // 16 * 16
+        region = torch.empty(nbytes * len(items) // 4, dtype=torch.int32, device=dev)
+        base = region.data_ptr()
+
+        def probe_fn():
+            for i in range(len(items)):
+                w4.read_probe_raw(base + i * nbytes, nbytes, sink.data_ptr(), PROBE_BLOCKS, handle)
+        g_us = graph_ms(torch, gemm_fn, stream, 10) * 1e3 / len(items)
+        p_us = graph_ms(torch, probe_fn, stream, 10) * 1e3 / len(items)
+        del region
+        wb = items[0][0].weight_bytes
+        out.append({"M": M, "K": K, "N": N, "bits": bits, "a4": a4, "copies": len(items),
+                    "gemm_us": round(g_us, 3), "probe_us": round(p_us, 3),
+                    "gemm_gbs": round(wb / g_us / 1e3, 1), "probe_gbs": round(wb / p_us / 1e3, 1),
+                    "gemm_over_probe": round(p_us / g_us, 4)})
+        log(f"shape {M}x{K}x{N}: GEMM {g_us:.2f} us, probe {p_us:.2f} us per launch ({len(items)} copies)")
+    return out
 
 
 def log(msg):
@@ -198,20 +272,26 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one HIP event between consecutive replays: the timed region is first to last event,
+    # and each replay's own duration gives the median and the minimum
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
-        ev0.record(stream)
-        for _ in range(args.steps):
+        evs[0].record(stream)
+        for i in range(args.steps):
             run_step()
-        ev1.record(stream)
+            evs[i + 1].record(stream)
     torch.cuda.synchronize()
+    ev0, ev1 = evs[0], evs[-1]
     elapsed_ms = ev0.elapsed_time(ev1)
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
+    ms_min = per_step[0]
     ms_per_step = elapsed_ms / args.steps
     gbs = wl.weight_bytes / (ms_per_step * 1e-3) / 1e9
     tflops = wl.flops / (ms_per_step * 1e-3) / 1e12
-    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, {gbs:.1f} GB/s, {tflops:.2f} TFLOP/s")
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step (median {ms_median:.4f}, min {ms_min:.4f}), "
+        f"{gbs:.1f} GB/s, {tflops:.2f} TFLOP/s")
 
     # Roofline figures of the dominant kernel.  The bound follows the step's arithmetic
     # intensity against the ridge of the two peaks (2*M flops per 0.5234375 weight bytes:
@@ -278,6 +358,26 @@ def main():
         log(f"streaming-read ceiling: {cgbs:.1f} GB/s ({probe_ms:.4f} ms per step); GEMM step at "
             f"{100 * gbs / cgbs:.1f}% of it")
         del pgraph, region
+        # The same probe as one launch over 1 GiB: the streaming rate without per-launch costs.
+        big = ONE_LAUNCH_PROBE_BYTES
+        bufb = torch.empty(big // 4, dtype=torch.int32, device=dev)
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                w4.read_probe_raw(bufb.data_ptr(), big, sink.data_ptr(), PROBE_BLOCKS, handle)
+            ev0.record(stream)
+            for _ in range(5):
+                w4.read_probe_raw(bufb.data_ptr(), big, sink.data_ptr(), PROBE_BLOCKS, handle)
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        one_ms = ev0.elapsed_time(ev1) / 5
+        ceiling["one_launch"] = {"bytes": big, "value": round(big / (one_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                                 "ms": round(one_ms, 4), "blocks": PROBE_BLOCKS}
+        ceiling["one_launch"]["frac_of_peak"] = round(ceiling["one_launch"]["value"] / HBM_PEAK_GBS, 4)
+        log(f"one-launch probe over {big / 2**30:.0f} GiB: {ceiling['one_launch']['value']} GB/s")
+        del bufb
+        # Per GEMM shape of the step: the GEMMs of that shape alone, and the probe over their
+        # byte counts, each captured and replayed like the step (one launch per GEMM).
+        ceiling["per_shape"] = per_shape_ceilings(args, gemms, calls, stream, sink, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -299,6 +399,7 @@ def main():
             done += 1
         dt = time.perf_counter() - t1
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "cpu_model": cpu_model(),
                "sample": f"{done} GEMMs of {args.workload} in step order, wrapping round the step "
                          f"({done / len(host_sample):.2f} steps of {len(host_sample)} GEMMs; every output element), "
                          f"{nbytes / 1e6:.1f} MB of weights in {dt:.2f} s"}
@@ -312,6 +413,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_median": round(ms_median, 5),
+        "ms_per_step_min": round(ms_min, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -25,10 +25,16 @@
  * M >= 64, and 17 <= M < 64 with K*N >= 2^25, run on the bfloat16 matrix cores with A
  * used as given.  Other shapes run on the
  * binary16 matrix cores with A rescaled by a power of two per (row, 128-wide group), so
- * that the group's largest |A| lands in [2^15, 2^16); elements more than 2^33 below that
- * maximum are rounded to the binary16 subnormal grid (an absolute error below 2^-40 of
- * the maximum per element, far inside the contract for any activation whose dynamic range
- * within 128 consecutive values is under about 2^30).
+ * that the group's largest |A| lands in [2^15, 2^16).  The contract above then holds for
+ * every activation row whose magnitudes within each 128-wide group span at most 2^32
+ * (largest |A| over smallest nonzero |A|): every such element is exact in binary16 after
+ * scaling.  Beyond that span the contract is replaced by a documented bound: an element
+ * whose binary exponent is more than 32 below that of its group's largest magnitude amax
+ * is rounded to the binary16 subnormal grid, an absolute error of at most 2^-40 * amax, so
+ *     |C - C_exact| <= 1e-4 * sum_k |A W| + 1e-6 + 2^-40 * sum_k' amax[m, g(k')] |W[k',n]|
+ * with k' over those elements.  A group whose largest magnitude is below about 2^-100 can
+ * lose bits in the float32 rescale; its whole contribution is then below 2^-90 and inside
+ * the 1e-6 term.
  *
  * All entry points validate their arguments on the host before any HIP call and return a
  * status; launches are asynchronous on the given stream (NULL = the null stream), so device
@@ -51,9 +57,11 @@ typedef enum w4_status {
     W4_ERR_ALIGN = 3,     /* a pointer is not aligned as required                           */
     W4_ERR_DEVICE = 4,    /* no HIP device, or the current device is not gfx950            */
     W4_ERR_HIP = 5,       /* a HIP runtime call or launch failed; see w4_last_error()      */
-    W4_ERR_WORKSPACE = 6  /* the split-K workspace would have to grow while the stream is
+    W4_ERR_WORKSPACE = 6, /* the split-K workspace would have to grow while the stream is
                              being captured into a graph: run the same shape once before
                              capturing                                                      */
+    W4_ERR_PLAN = 7       /* internal: the launch plan names no compiled kernel instance
+                             (nothing was launched; C is not written)                      */
 } w4_status;
 
 /*
@@ -64,9 +72,15 @@ typedef enum w4_status {
  *   A_bf16, Wq and C must be 16-byte aligned (W4_ERR_ALIGN otherwise); scales_f16 2-byte.
  *   Any N is accepted; N % 4 == 0 with 8-byte aligned scales and 4-byte aligned zeros
  *   takes the vectorized load path.
- *   Split-K shapes use a library workspace owned per (device, stream): it is allocated on
- *   first need (outside graph capture) and kept until the process ends.  Calls that may run
- *   concurrently on different streams each get their own workspace.
+ *   Split-K shapes use a library workspace (arrival counters and float32 partials) owned
+ *   per (device, stream): it is allocated on first need (outside graph capture, so a graph
+ *   must not capture the first call of a new split shape) and kept until the process ends.
+ *   Calls issued on different streams each get their own workspace and may overlap.  A
+ *   captured graph keeps the workspace of the stream it was captured on: replay it only
+ *   where it cannot overlap other work that uses that same workspace (other calls or graphs
+ *   issued on, or captured on, that stream); capture graphs that may run concurrently on
+ *   distinct streams.  Overlapping users of one workspace race on its counters and give
+ *   wrong results without an error.
  *   stream: a hipStream_t, or NULL.
  */
 w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_f16,
@@ -129,7 +143,10 @@ w4_status a4_quantize(const void *A_bf16, uint32_t *Aq, float *A_scales, int64_t
 w4_status w8_pack(const uint8_t *q_u8, uint32_t *Wq8, int64_t K, int64_t N, void *stream);
 
 /*
- * Packs 4-bit codes into the storage layout: Wq[kb,n] = sum_j (q[8kb+j,n] & 0xF) << 4j.
+ * Packs 4-bit codes into the storage layout of the INT4 GPTQ weights that "When Do
+ * Quantized Drafts Help Speculative Decoding?" ("Current pilot setup") runs its draft on
+ * (the page names the format, not the bit order; this layout is the sequential reading,
+ * eight codes per word along K): Wq[kb,n] = sum_j (q[8kb+j,n] & 0xF) << 4j.
  *   q_u4: [K, N] bytes (high nibbles ignored); Wq: [K/8, N] uint32, overwritten.
  *   K >= 8 with K % 8 == 0, N >= 1; Wq must be 4-byte aligned.  Bit-exact.
  */

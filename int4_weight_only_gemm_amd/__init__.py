@@ -42,6 +42,7 @@ STATUS = {
     4: "W4_ERR_DEVICE",
     5: "W4_ERR_HIP",
     6: "W4_ERR_WORKSPACE",
+    7: "W4_ERR_PLAN",
 }
 
 

@@ -104,7 +104,12 @@ __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f
 __device__ __forceinline__ uint32_t as_u(f16x2 h) { return __builtin_bit_cast(uint32_t, h); }
 
 // Eight codes of one packed word -> eight exact binary16 values (q_j - z), in the order
-// j = 0,4,1,5,2,6,3,7 (element e holds nibble (e >> 1) + 4 * (e & 1)).
+// j = 0,4,1,5,2,6,3,7 (element e holds nibble (e >> 1) + 4 * (e & 1)).  This is the
+// published magic-number integer-to-float conversion (Kim et al. 2022, "Who Says Elephants
+// Can't Run?", for FasterTransformer's mixed-precision GEMMs; also used by Marlin): an
+// integer placed in the low mantissa bits of a float whose exponent makes the mantissa unit
+// 1, here binary16 1024.0, then that float's value subtracted in one float add.  Here the
+// per-column zero point is folded into the subtrahend.
 //   zlo = fp16 pair of -(1024 + z), zhi = fp16 pair of -(64 + z).
 //   magic = 0x64006400 (binary16 1024.0 in both halves), held in a VGPR so that each
 //   mask-and-insert is one v_and_or_b32 (VOP3 takes one SGPR/literal operand on gfx9).
@@ -625,8 +630,18 @@ void w4a16_kernel(SmallParams p)
             if (row0 + ps * kRowsPerPass < mv) store_c(row0 + ps * kRowsPerPass, sum[ps]);
         return;
     }
-    // Partials travel as 16-byte device-coherent stores and loads (the cache policy of
-    // agent-scope atomics), one per lane, pass and split.
+    // Split-K handoff.  Writer side: every split stores its partial tile with device-scope
+    // stores (the ISA's sc1 scope bit: written through to the device coherence point, one
+    // 16-byte store per lane and pass); each wave waits until its stores are complete, the
+    // workgroup barrier then orders all of them before thread 0's increment of the tile's
+    // arrival counter (agent scope).  Reader side: the workgroup whose increment returns
+    // splits - 1 is the last arriver; it takes an agent-scope acquire fence (invalidating its
+    // non-coherent cache lines, and no later load may be moved above it), its second barrier
+    // orders that fence before all of its waves' loads of the partials (device-scope loads),
+    // and it sums them in split order, writes C and resets the counter for the next call
+    // (ordered by the kernel boundary).  A release fence at agent scope in every writer (an
+    // L2 write-back per workgroup) measured 8% slower on the M = 5 verify step and adds
+    // nothing for stores that already carry device scope.
     const uint32_t stile = tile - nfull;  // index among the split tiles
     const int64_t split_tiles = (int64_t)p.m_blocks * p.n_tiles - nfull;
     constexpr uint32_t kPartBytes = kRows * kTileN * 4;  // one split's partial tile
@@ -641,15 +656,15 @@ void w4a16_kernel(SmallParams p)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, sum[ps]), prs,
                                                    lane_part(row) + (uint32_t)sp * kPartBytes, 0, kCacheCoherent);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores are complete
     __syncthreads();
     if (threadIdx.x == 0) {
         const unsigned prev = __hip_atomic_fetch_add(p.count + stile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (unsigned)(p.splits - 1));
+        if (s_last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!s_last) return;
-    asm volatile("" ::: "memory");
 #pragma unroll
     for (int ps = 0; ps < kPasses; ++ps) {
         const int row = row0 + ps * kRowsPerPass;
@@ -1530,10 +1545,38 @@ size_t plan_lds_bytes(int64_t M, const w4_plan &pl)
     return tiles > red ? tiles : red;
 }
 
+// The small-M instances compiled below: 16-row blocks (one activation chunk row per 4 rows,
+// av = 1..4) for every code width and activation type, and 32-row blocks (av = 5..8) for
+// 4-bit activations only.  A plan outside this set is an internal error, reported as
+// W4_ERR_PLAN before anything is launched.
+bool small_instance_exists(int rb, int av, int bits, bool a4)
+{
+    if (rb == 1) return av >= 1 && av <= 4 && (bits == 4 || (bits == 8 && !a4));
+    return rb == 2 && a4 && bits == 4 && av >= 5 && av <= 8;
+}
+
+// Whether a plan names a compiled kernel: every large-M row-tile count (1..5) is compiled;
+// small-M plans are checked against the instance table above.
+bool plan_has_instance(int64_t M, const w4_plan &pl, int bits, bool a4)
+{
+    if (pl.kernel == 3) return !a4 && bits == 4 && pl.tile_m >= 1 && pl.tile_m <= kLMaxRT * 32;
+    if (pl.tile_m % kTileM != 0) return false;
+    const int rows = M < pl.tile_m ? (int)M : pl.tile_m;
+    return small_instance_exists(pl.tile_m / kTileM, (rows + 3) / 4, bits, a4);
+}
+
+w4_status check_plan(const char *name, int64_t M, const w4_plan &pl, int bits, bool a4)
+{
+    if (plan_has_instance(M, pl, bits, a4)) return W4_OK;
+    set_error("%s: internal error: plan (kernel %d, %d-row blocks) for M=%lld has no compiled instance", name,
+              pl.kernel, pl.tile_m, (long long)M);
+    return W4_ERR_PLAN;
+}
+
 // Small-M launches: one instantiation per (vectorized loads, waves, activation chunks per
 // lane, code width); every shape keeps 3 waves per SIMD.
 template <int BITS, bool A4>
-void launch_small(bool tall, int rb, int av, bool vec, dim3 grid, size_t lds, hipStream_t s, const SmallParams &p)
+bool launch_small(bool tall, int rb, int av, bool vec, dim3 grid, size_t lds, hipStream_t s, const SmallParams &p)
 {
 #define W4_LAUNCH(V, WV, AVV, OCCV, RBV) \
     hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, OCCV, BITS, A4, RBV>), grid, dim3(WV * kWave), lds, s, p)
@@ -1543,6 +1586,7 @@ void launch_small(bool tall, int rb, int av, bool vec, dim3 grid, size_t lds, hi
 #define W4_LAUNCH_32(V, WV) \
     switch (av) { case 5: W4_LAUNCH(V, WV, 5, kOccupancy2, 2); break; case 6: W4_LAUNCH(V, WV, 6, kOccupancy2, 2); break; \
                   case 7: W4_LAUNCH(V, WV, 7, kOccupancy2, 2); break; default: W4_LAUNCH(V, WV, 8, kOccupancy2, 2); break; }
+    if (!small_instance_exists(rb, av, BITS, A4)) return false;
     if (rb == 1) {
         if (tall) { if (vec) { W4_LAUNCH_16(true, kTall.waves) } else { W4_LAUNCH_16(false, kTall.waves) } }
         else { if (vec) { W4_LAUNCH_16(true, kWide.waves) } else { W4_LAUNCH_16(false, kWide.waves) } }
@@ -1550,6 +1594,7 @@ void launch_small(bool tall, int rb, int av, bool vec, dim3 grid, size_t lds, hi
         if (tall) { if (vec) { W4_LAUNCH_32(true, kTall2.waves) } else { W4_LAUNCH_32(false, kTall2.waves) } }
         else { if (vec) { W4_LAUNCH_32(true, kWide2.waves) } else { W4_LAUNCH_32(false, kWide2.waves) } }
     }
+    return true;
 #undef W4_LAUNCH_32
 #undef W4_LAUNCH_16
 #undef W4_LAUNCH
@@ -1585,6 +1630,8 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         make_small_plan(M, K, N, &pl, bits, a4);
     else
         make_plan(M, K, N, &pl);
+    st = check_plan(name, M, pl, bits, a4);
+    if (st != W4_OK) return st;
     hipStream_t s = (hipStream_t)stream;
     unsigned *count = nullptr;
     float *part = nullptr;
@@ -1656,12 +1703,14 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         const int rows = M < pl.tile_m ? (int)M : pl.tile_m;
         const int av = (rows + 3) / 4;
         const bool tall = pl.kernel == 2 || pl.kernel == 5 || pl.kernel == 7;
-        if (a4)
-            launch_small<4, true>(tall, rb, av, vec, grid, lds, s, p);
-        else if (bits == 8)
-            launch_small<8, false>(tall, rb, av, vec, grid, lds, s, p);
-        else
-            launch_small<4, false>(tall, rb, av, vec, grid, lds, s, p);
+        const bool launched = a4 ? launch_small<4, true>(tall, rb, av, vec, grid, lds, s, p)
+                              : bits == 8 ? launch_small<8, false>(tall, rb, av, vec, grid, lds, s, p)
+                                          : launch_small<4, false>(tall, rb, av, vec, grid, lds, s, p);
+        if (!launched) {
+            set_error("%s: internal error: plan (kernel %d, %d-row blocks, %d chunk rows) has no compiled "
+                      "instance", name, pl.kernel, pl.tile_m, av);
+            return W4_ERR_PLAN;
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(name, e);
@@ -1682,6 +1731,7 @@ const char *w4_status_string(w4_status s)
     case W4_ERR_DEVICE: return "no gfx950 device";
     case W4_ERR_HIP: return "HIP runtime error";
     case W4_ERR_WORKSPACE: return "workspace cannot grow during stream capture";
+    case W4_ERR_PLAN: return "internal error: no kernel instance for the launch plan";
     }
     return "unknown status";
 }
@@ -1697,7 +1747,7 @@ w4_status w4a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out)
     w4_status st = validate_gemm_shape(M, K, N);
     if (st != W4_OK) return st;
     make_plan(M, K, N, out);
-    return W4_OK;
+    return check_plan("w4a16_plan", M, *out, 4, false);
 }
 
 w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_f16,
@@ -1729,7 +1779,7 @@ w4_status w4a4_plan(int64_t M, int64_t K, int64_t N, w4_plan *out)
     w4_status st = validate_gemm_shape(M, K, N, 4, true);
     if (st != W4_OK) return st;
     make_small_plan(M, K, N, out, 4, true);
-    return W4_OK;
+    return check_plan("w4a4_plan", M, *out, 4, true);
 }
 
 w4_status a4_quantize(const void *A_bf16, uint32_t *Aq, float *A_scales, int64_t M, int64_t K, void *stream)
@@ -1771,7 +1821,7 @@ w4_status w8a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out)
     w4_status st = validate_gemm_shape(M, K, N, 8);
     if (st != W4_OK) return st;
     make_small_plan(M, K, N, out, 8);
-    return W4_OK;
+    return check_plan("w8a16_plan", M, *out, 8, false);
 }
 
 w4_status w4_quantize(const void *W_f16, uint32_t *Wq, void *scales_f16, uint8_t *zeros_u4, int64_t K, int64_t N,

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         s = w4.status_string(code)
         assert s and s != "unknown status"
     assert w4.status_string(99) == "unknown status"
@@ -214,6 +214,19 @@ def test_plan_covers_shapes():
                 assert p["workgroups"] <= 256 * per_cu or p["splits"] == 1
     with pytest.raises(w4.W4Error):
         w4.plan(5, 100, 64)
+
+
+def test_every_plan_has_a_kernel_instance():
+    # the plan entry points run the same instance check as the GEMM entry points (which
+    # return W4_ERR_PLAN before launching anything): every plan the planners emit, for every
+    # row count up to the bf16 kernel's range and beyond, names a compiled kernel
+    for M in list(range(1, 80)) + [96, 128, 160, 161, 200, 320]:
+        for K, N in ((128, 3), (1536, 1536), (3584, 4608), (3584, 37888), (18944, 3584), (4096, 22016)):
+            for bits, a4 in ((4, False), (8, False), (4, True)):
+                p = w4.plan(M, K, N, bits=bits, a4=a4)  # raises W4Error(W4_ERR_PLAN) otherwise
+                if p["kernel"] != 3:
+                    rows = min(M, p["tile_m"])
+                    assert p["tile_m"] == 16 or (p["tile_m"] == 32 and a4 and 5 <= (rows + 3) // 4 <= 8)
 
 
 @pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present")
