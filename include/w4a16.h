@@ -59,7 +59,8 @@ typedef enum w4_status {
     W4_ERR_HIP = 5,       /* a HIP runtime call or launch failed; see w4_last_error()      */
     W4_ERR_WORKSPACE = 6, /* the split-K workspace would have to grow while the stream is
                              being captured into a graph: run the same shape once before
-                             capturing                                                      */
+                             capturing; or (w4a16_gemm_noalloc) the plan needs more scratch
+                             than its fixed maximum                                        */
     W4_ERR_PLAN = 7       /* internal: the launch plan names no compiled kernel instance
                              (nothing was launched; C is not written)                      */
 } w4_status;
@@ -86,6 +87,27 @@ typedef enum w4_status {
 w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_f16,
                      const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N,
                      void *stream);
+
+/*
+ * w4a16_gemm for callers that cannot allocate device memory: code under HIP graph capture
+ * (including a first call of a new split shape), tight serving loops, or harnesses that
+ * forbid hipMalloc.  Same arguments, layouts, plan, kernels and results (bit for bit) as
+ * w4a16_gemm, but the split-K scratch is a fixed array of 64 MiB per GPU inside the library
+ * (its code object's zero-initialized data, held by every GPU the library is loaded on until
+ * the process ends), not a workspace: the call makes no hipMalloc, hipFree or other
+ * allocating call.  The first call on a device looks up that array's address and clears its
+ * arrival counters with a kernel on `stream`.
+ *   A shape whose plan needs more than 65536 arrival counters or more than 64 MiB - 256 KiB
+ *   of partials (in practice large M with deep K splits, e.g. M * N * splits * 4 bytes
+ *   beyond that) returns W4_ERR_WORKSPACE before anything is launched.
+ *   Every call on one GPU shares that GPU's array: calls (and graphs holding calls) that
+ *   overlap in time on one GPU race on its counters and partials and can return wrong C
+ *   without an error.  Serialize them (for example, one stream).
+ *   Other errors as for w4a16_gemm.
+ */
+w4_status w4a16_gemm_noalloc(const void *A_bf16, const uint32_t *Wq, const void *scales_f16,
+                             const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N,
+                             void *stream);
 
 /*
  * C = A . W for the 8-bit variant of the format (W8A16): the GPTQ INT8 draft that "When

@@ -76,6 +76,8 @@ _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _lib.w4a16_gemm.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.w4a16_gemm.restype = ctypes.c_int
+_lib.w4a16_gemm_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp]
+_lib.w4a16_gemm_noalloc.restype = ctypes.c_int
 _lib.w4_pack.argtypes = [_vp, _vp, _i64, _i64, _vp]
 _lib.w4_pack.restype = ctypes.c_int
 _lib.w4_quantize.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _vp]
@@ -187,6 +189,15 @@ def gemm(A, Wq, scales, zeros, out=None, stream=None, bits: int = 4):
     if rc:
         raise W4Error(rc, name)
     return out
+
+
+def gemm_noalloc_raw(A_ptr: int, Wq_ptr: int, S_ptr: int, Z_ptr: int, C_ptr: int, M: int, K: int, N: int,
+                     stream_handle: int = 0) -> None:
+    """w4a16_gemm_noalloc on raw device pointers: the 4-bit GEMM with the library's fixed
+    per-GPU scratch instead of an allocated workspace (no device allocation at all)."""
+    rc = _lib.w4a16_gemm_noalloc(A_ptr, Wq_ptr, S_ptr, Z_ptr, C_ptr, M, K, N, stream_handle)
+    if rc:
+        raise W4Error(rc, "w4a16_gemm_noalloc")
 
 
 def quantize_activations(A, stream=None):

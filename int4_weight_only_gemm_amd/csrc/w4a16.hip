@@ -1273,6 +1273,67 @@ w4_status get_workspace(int dev, hipStream_t stream, size_t tiles, size_t part_b
     return W4_OK;
 }
 
+// Scratch for the entry point that allocates nothing (w4a16_gemm_noalloc): a file-scope
+// device array with the workspace's layout, [arrival counters][partials], fixed for the life
+// of the process.  In host code `scratch` is only a stand-in for the symbol: its device
+// address differs per GPU and is looked up once per device (hipGetSymbolAddress, with that
+// device current) and used in its place everywhere.  The counters must be zero between calls:
+// they are zero when the code object is loaded, every call's last arrivers reset the ones it
+// used, and the set-up clears them once more with a fill kernel (no memset node, so a set-up
+// that happens under stream capture is replayed safely).
+constexpr size_t kScratchCounters = 1 << 16;                  // arrival counters, 256 KiB
+constexpr size_t kScratchCounterBytes = kScratchCounters * 4;
+constexpr size_t kScratchBytes = (size_t)64 << 20;           // 64 MiB per GPU in all
+constexpr size_t kScratchPartBytes = kScratchBytes - kScratchCounterBytes;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void w4_fill_zero_kernel(uint32_t *__restrict__ p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+char *g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch` per GPU, set once
+
+// Set-up on the entry point's first call on a device (with that device current): look up the
+// array's device address and clear its counters on the caller's stream.
+w4_status setup_scratch(int dev, hipStream_t stream)
+{
+    if (dev < 0 || dev >= kMaxDevices) {
+        set_error("w4a16_gemm_noalloc: device %d is beyond the %d this library tracks", dev, kMaxDevices);
+        return W4_ERR_DEVICE;
+    }
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_scratch_ptr[dev]) return W4_OK;
+    void *ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail("hipGetSymbolAddress(scratch)", e);
+    if (!ptr) {
+        set_error("hipGetSymbolAddress(scratch) returned a null address on device %d", dev);
+        return W4_ERR_HIP;
+    }
+    hipLaunchKernelGGL(w4_fill_zero_kernel, dim3(256), dim3(256), 0, stream, (uint32_t *)ptr,
+                       (int64_t)kScratchCounters);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail("scratch set-up launch", e);
+    g_scratch_ptr[dev] = (char *)ptr;
+    return W4_OK;
+}
+
+// The scratch regions for one call's plan, or an error when the plan needs more than the
+// array holds (nothing is launched then).
+w4_status get_scratch(int dev, size_t tiles, size_t part_bytes, unsigned **count, float **part)
+{
+    if (tiles > kScratchCounters || part_bytes > kScratchPartBytes) {
+        set_error("w4a16_gemm_noalloc: the plan needs %zu arrival counters and %zu partial bytes; the fixed "
+                  "scratch holds %zu counters and %zu bytes", tiles, part_bytes, kScratchCounters, kScratchPartBytes);
+        return W4_ERR_WORKSPACE;
+    }
+    *count = (unsigned *)g_scratch_ptr[dev];
+    *part = (float *)(g_scratch_ptr[dev] + kScratchCounterBytes);
+    return W4_OK;
+}
+
 w4_status validate_gemm_shape(int64_t M, int64_t K, int64_t N, int bits = 4, bool a4 = false)
 {
     if (M < 1 || N < 1 || K < kGroup || K % kGroup != 0) {
@@ -1605,7 +1666,7 @@ bool launch_small(bool tall, int rb, int av, bool vec, dim3 grid, size_t lds, hi
 // scales.
 w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, const float *As, const uint32_t *Wq,
                    const void *scales_f16, const uint8_t *zeros, float *C, int64_t M, int64_t K, int64_t N,
-                   void *stream)
+                   void *stream, bool noalloc = false)
 {
     if (!A_bf16 || (a4 && !As) || !Wq || !scales_f16 || !zeros || !C) {
         set_error("%s: a required pointer is NULL", name);
@@ -1633,12 +1694,17 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
     st = check_plan(name, M, pl, bits, a4);
     if (st != W4_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (noalloc) {
+        st = setup_scratch(dev, s);
+        if (st != W4_OK) return st;
+    }
     unsigned *count = nullptr;
     float *part = nullptr;
     if (pl.workspace_bytes > 0) {
         // small-M: [tile counters][partial tiles]; large-M: [split slices] only
         const int64_t tiles = pl.kernel == 3 ? 0 : (int64_t)pl.n_tiles * pl.m_blocks - pl.full_tiles;
-        st = get_workspace(dev, s, (size_t)tiles, (size_t)(pl.workspace_bytes - tiles * 4), &count, &part);
+        st = noalloc ? get_scratch(dev, (size_t)tiles, (size_t)(pl.workspace_bytes - tiles * 4), &count, &part)
+                     : get_workspace(dev, s, (size_t)tiles, (size_t)(pl.workspace_bytes - tiles * 4), &count, &part);
         if (st != W4_OK) return st;
     }
     const dim3 grid((unsigned)pl.workgroups);
@@ -1755,6 +1821,13 @@ w4_status w4a16_gemm(const void *A_bf16, const uint32_t *Wq, const void *scales_
                      void *stream)
 {
     return run_gemm(4, false, "w4a16_gemm", A_bf16, nullptr, Wq, scales_f16, zeros_u4, C, M, K, N, stream);
+}
+
+w4_status w4a16_gemm_noalloc(const void *A_bf16, const uint32_t *Wq, const void *scales_f16,
+                             const uint8_t *zeros_u4, float *C, int64_t M, int64_t K, int64_t N, void *stream)
+{
+    return run_gemm(4, false, "w4a16_gemm_noalloc", A_bf16, nullptr, Wq, scales_f16, zeros_u4, C, M, K, N, stream,
+                    true);
 }
 
 w4_status w8a16_gemm(const void *A_bf16, const uint32_t *Wq8, const void *scales_f16,
