@@ -23,7 +23,7 @@
  *     |C - C_exact| <= 1e-4 * sum_k |A[m,k] * W[k,n]| + 1e-6.
  * The (q - z) factors and their products with A are exact; partial sums are float32.
  * M >= 64, and 17 <= M < 64 with K*N >= 2^25, run on the bfloat16 matrix cores with A
- * used as given.  Other shapes run on the
+ * used as given.  Other shapes (the small-M and narrow-tile kernels) run on the
  * binary16 matrix cores with A rescaled by a power of two per (row, 128-wide group), so
  * that the group's largest |A| lands in [2^15, 2^16).  The contract above then holds for
  * every activation row whose magnitudes within each 128-wide group span at most 2^32
@@ -219,11 +219,16 @@ typedef struct w4_plan {
                                3 = large-M (M >= 64, or M >= 17 with K*N >= 2^25:
                                    8 waves, bf16 MFMA),
                                4, 5 = 8-bit codes (w8a16_gemm), wide and tall as 1, 2,
-                               6, 7 = 4-bit activations (w4a4_gemm), wide and tall          */
-    int tile_m;             /* output rows per row block: 16 for kernels 1, 2, 4, 5; 16 for
-                               kernels 6, 7, except 32 at 17..32 rows; 1 to 160 for kernel
-                               3, computed in row tiles of 32                                */
-    int tile_n;             /* output columns per workgroup tile (64, or 256 for kernel 3)   */
+                               6, 7 = 4-bit activations (w4a4_gemm), wide and tall,
+                               8 = narrow tiles (M <= 16 with at most 64 groups, the
+                                   activations staged whole in at most 64 KiB of LDS, and at
+                                   most 256 tiles: 8 waves, one 16-column tile over all of
+                                   K per workgroup, fp16 MFMA, no K split)                    */
+    int tile_m;             /* output rows per row block: 16 for kernels 1, 2, 4, 5, 8; 16
+                               for kernels 6, 7, except 32 at 17..32 rows; 1 to 160 for
+                               kernel 3, computed in row tiles of 32                         */
+    int tile_n;             /* output columns per workgroup tile (64; 256 for kernel 3; 16
+                               for kernel 8)                                                 */
     int m_blocks;           /* row blocks of tile_m                                          */
     int n_tiles;            /* column tiles of tile_n                                        */
     int splits;             /* K splits across workgroups (1 = no workspace)                */

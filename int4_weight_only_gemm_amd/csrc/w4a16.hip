@@ -283,6 +283,7 @@ __device__ __forceinline__ void load_group(const SmallParams &p, const Resources
             for (int t = 0; t < 4; ++t) r.w[st][t] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, o.w[t], so, kCacheStream);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);  // the group's scales and zeros follow its own words
     const uint32_t gso = (uint32_t)g * (uint32_t)p.N;
     if (VEC) {
         r.s = __builtin_amdgcn_raw_buffer_load_b64(rs.S, o.s[0], gso * 2, 0);
@@ -307,13 +308,10 @@ __device__ __forceinline__ void load_group(const SmallParams &p, const Resources
 // chunks travel in the register ring with the group's weights, so the conversion overlaps
 // the loads still in flight and there is no workgroup-wide staging phase.
 
-template <int AV, int BITS, bool A4>
-struct PipeRegs {
-    u32x4 w[BITS];
-    u32x2 s;      // 4 binary16 scales
-    uint32_t z;   // 4 zero bytes
-    // activation chunks of rows 4i + lane/16, chunk lane%16 of the group: 8 bfloat16
-    // values, or (4-bit activations) one word of 8 codes and the row's scale bits
+// Activation chunks of rows 4i + lane/16, chunk lane%16 of the group: 8 bfloat16 values, or
+// (4-bit activations) one word of 8 codes and the row's scale bits.
+template <int AV, bool A4>
+struct ActRegs {
     typename std::conditional<A4, u32x2, u32x4>::type a[AV];
 };
 
@@ -322,13 +320,10 @@ struct PipeRegs {
 constexpr int pipe_wave_bytes(int rb) { return rb * (kTileM * kARowBytes + kTileM * 4); }
 constexpr int pipe_exp_offset(int rb) { return rb * kTileM * kARowBytes; }
 
-template <bool VEC, int AV, int BITS, bool A4>
-__device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources &rs, const LaneOffsets<VEC> &o,
-                                          const uint32_t (&aoff)[AV], const uint32_t (&asoff)[AV], int g,
-                                          PipeRegs<AV, BITS, A4> &r)
+template <int AV, bool A4>
+__device__ __forceinline__ void load_act(const Resources &rs, const uint32_t (&aoff)[AV], const uint32_t (&asoff)[AV],
+                                         int g, ActRegs<AV, A4> &r)
 {
-    // activations first: their conversion needs only them, and can run while the
-    // weights are still in flight (loads complete in issue order)
 #pragma unroll
     for (int i = 0; i < AV; ++i) {
         if constexpr (A4) {
@@ -338,12 +333,6 @@ __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources 
             r.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[i], (uint32_t)g * (kGroup * 2), 0);
         }
     }
-    GroupRegs<BITS> w;
-    load_group<VEC, BITS>(p, rs, o, g, w);
-#pragma unroll
-    for (int st = 0; st < BITS; ++st) r.w[st] = w.w[st];
-    r.s = w.s;
-    r.z = w.z;
 }
 
 // Convert this wave's group of activations into its LDS tile: row r scaled by 2^x[r],
@@ -352,7 +341,7 @@ __device__ __forceinline__ void load_pipe(const SmallParams &p, const Resources 
 // unpacked instead (offset-binary codes, zero point 8, exact in binary16, in the weight
 // operand's element order) and the row's float32 scale is stored in place of x[r].
 template <int AV, int BITS, bool A4, int RB>
-__device__ __forceinline__ void stage_pipe(const PipeRegs<AV, BITS, A4> &r, char *lds_wave, int mv, int lane)
+__device__ __forceinline__ void stage_pipe(const ActRegs<AV, A4> &r, char *lds_wave, int mv, int lane)
 {
     constexpr int kExpOffset = pipe_exp_offset(RB);
     asm volatile("" ::: "memory");  // the previous group's LDS reads stay before these writes
@@ -382,7 +371,7 @@ __device__ __forceinline__ void stage_pipe(const PipeRegs<AV, BITS, A4> &r, char
 }
 
 template <int AV, int BITS, bool A4, int RB>
-__device__ __forceinline__ void compute_pipe(const PipeRegs<AV, BITS, A4> &r, const char *lds_wave, int mv, int lane,
+__device__ __forceinline__ void compute_pipe(const GroupRegs<BITS> &r, const char *lds_wave, int mv, int lane,
                                              f32x4 (&acc)[RB][4])
 {
     constexpr int kExpOffset = pipe_exp_offset(RB);
@@ -557,31 +546,38 @@ void w4a16_kernel(SmallParams p)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[rb][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // Two register slots: group j+1 (weights and activations) is in flight while group j is
-    // converted and computed.
+    // Two register slots: group j+1 (its activations, then its weights) is in flight while
+    // group j is converted and computed; unrolled by two with an exact tail, so every load is
+    // issued once and none sits behind a branch.
     auto G = [&](int j) { return g0 + WAVES * j; };
-    auto run = [&](const PipeRegs<AV, BITS, A4> &r) {
-        stage_pipe<AV, BITS, A4, RB>(r, tile_lds, mv, lane);
-        compute_pipe<AV, BITS, A4, RB>(r, tile_lds, mv, lane, acc);
-    };
-    if (n_my > 0) {
-        PipeRegs<AV, BITS, A4> r0, r1;
-        load_pipe<VEC, AV, BITS, A4>(p, rs, lo, aoff, asoff, G(0), r0);
+    auto run_loop = [&]() {
+        GroupRegs<BITS> w0, w1;
+        ActRegs<AV, A4> a0, a1;
+        auto load2 = [&](int j, GroupRegs<BITS> &w, ActRegs<AV, A4> &a) {
+            load_act<AV, A4>(rs, aoff, asoff, G(j), a);
+            load_group<VEC, BITS>(p, rs, lo, G(j), w);
+        };
+        auto run1 = [&](const GroupRegs<BITS> &w, const ActRegs<AV, A4> &a) {
+            stage_pipe<AV, BITS, A4, RB>(a, tile_lds, mv, lane);
+            compute_pipe<AV, BITS, A4, RB>(w, tile_lds, mv, lane, acc);
+        };
+        load2(0, w0, a0);
         int j = 0;
         for (; j + 2 < n_my; j += 2) {
-            load_pipe<VEC, AV, BITS, A4>(p, rs, lo, aoff, asoff, G(j + 1), r1);
-            run(r0);
-            load_pipe<VEC, AV, BITS, A4>(p, rs, lo, aoff, asoff, G(j + 2), r0);
-            run(r1);
+            load2(j + 1, w1, a1);
+            run1(w0, a0);
+            load2(j + 2, w0, a0);
+            run1(w1, a1);
         }
         if (j + 1 < n_my) {
-            load_pipe<VEC, AV, BITS, A4>(p, rs, lo, aoff, asoff, G(j + 1), r1);
-            run(r0);
-            run(r1);
+            load2(j + 1, w1, a1);
+            run1(w0, a0);
+            run1(w1, a1);
         } else {
-            run(r0);
+            run1(w0, a0);
         }
-    }
+    };
+    if (n_my > 0) run_loop();
 
     // Reduce the waves' accumulators through LDS in wave order (reproducible).
     __syncthreads();
@@ -688,6 +684,217 @@ void w4a16_kernel(SmallParams p)
         }
     }
     if (threadIdx.x == 0) __hip_atomic_store(p.count + stile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------------------------------
+// Narrow-tile kernel (M <= 16, activations small enough to stage whole in LDS): one
+// workgroup per 16-column tile, over all of K, so narrow outputs fill the GPU without a
+// K split across workgroups and without its handoff.
+//  * Prologue: each wave issues the weight loads of all its groups (4-byte loads: lane
+//    (c, kq) reads packed row 4 st + kq of column c, so 16 lanes read 64 contiguous bytes
+//    per row), then the workgroup converts the whole activation block A[M, K] once into
+//    LDS as binary16, each (row, group) scaled by its own power of two as in the small-M
+//    kernel (one 16-lane DPP row per (row, group)), and stores the exponents beside it.
+//  * Main loop: wave w computes groups w, w + WAVES, ...: per group four 16x16x32 f16
+//    matrix-core steps with the lane's unpacked word as B operand and A from LDS (rows
+//    M.. read a zero chunk), then the float32 rescale by ldexp(s, -x).
+//  * The waves' partial sums are added through LDS in wave order and written to C.
+// Neighbouring tiles run on one XCD, so the two halves of each 128-byte line of a packed
+// row are read through the same L2.
+
+constexpr int kNarrowN = 16;  // output columns per workgroup
+constexpr int kNarrowMaxGroups = 8;  // groups per wave held in registers at once
+
+struct NarrowParams {
+    const uint16_t *A;
+    const uint32_t *Wq;
+    const uint16_t *S;
+    const uint8_t *Z;
+    float *C;
+    int64_t M, K, N;
+    int groups;
+    int n_tiles;
+};
+
+// LDS layout of the narrow kernel: activation rows [groups][M][kARowBytes] (binary16, row
+// pitch padded for conflict-free reads), one zero chunk, then the exponents [groups][16].
+__host__ __device__ constexpr int narrow_zero_offset(int groups, int M) { return groups * M * kARowBytes; }
+__host__ __device__ constexpr int narrow_exp_offset(int groups, int M) { return groups * M * kARowBytes + 16; }
+__host__ __device__ constexpr int narrow_lds_bytes(int groups, int M, int waves)
+{
+    const int stage = narrow_exp_offset(groups, M) + groups * kTileM * 4;
+    const int red = waves * M * kNarrowN * 4;
+    return stage > red ? stage : red;
+}
+
+struct NarrowW {
+    uint32_t w[4];  // packed rows 4 st + kq of the lane's column, st = 0..3
+    uint32_t s;     // binary16 scale (low half)
+    uint32_t z;     // zero byte
+};
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(NarrowParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int tile = (int)xcd_local_id(blockIdx.x, gridDim.x);
+    const int n0 = tile * kNarrowN;
+    const int M = (int)p.M, G = p.groups;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int c = lane & 15, kq = lane >> 4;
+    const int64_t N = p.N;
+    const int64_t nc = n0 + c < N ? n0 + c : N - 1;  // clamped column for loads
+
+    Resources rs;
+    rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K / 8 * N * 4), kRsrcWord3);
+    rs.S = __builtin_amdgcn_make_buffer_rsrc((void *)p.S, (short)0, (int)(p.K / kGroup * N * 2), kRsrcWord3);
+    rs.Z = __builtin_amdgcn_make_buffer_rsrc((void *)p.Z, (short)0, (int)(p.K / kGroup * N), kRsrcWord3);
+    rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(p.M * p.K * 2), kRsrcWord3);
+    const uint32_t woff = (uint32_t)(((int64_t)kq * N + nc) * 4);
+    const uint32_t rowbytes = (uint32_t)N * 4;
+
+    const int n_my = wave < G ? (G - wave + WAVES - 1) / WAVES : 0;
+    auto load_w = [&](int g, NarrowW &r) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            r.w[st] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, woff, ((uint32_t)g * 16 + 4 * st) * rowbytes, kCacheStream);
+        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs.S, (uint32_t)(nc * 2), (uint32_t)g * (uint32_t)N * 2, 0);
+        r.z = __builtin_amdgcn_raw_buffer_load_b8(rs.Z, (uint32_t)nc, (uint32_t)g * (uint32_t)N, 0);
+    };
+
+    // Stage A: pair q = g * M + m is (row m, group g); DPP row d of the workgroup takes
+    // pairs d, d + 4 WAVES, ...  Lane kc of a DPP row holds values 8 kc .. 8 kc + 7.
+    const int pairs = G * M;
+    const int dpp_rows = 4 * WAVES;
+    const int drow = threadIdx.x >> 4, kc = lane & 15;
+    // q = g * M + m split without an integer division: q < 16 * 64 (the plan keeps M <= 16
+    // and at most 64 groups), (q + 0.5) * inv_m in float32 is within 2^-22 of (q + 0.5) / M,
+    // and that quotient's fraction is at least 1/(2M) >= 1/32 away from an integer, so the
+    // truncation gives g exactly
+    const float inv_m = 1.0f / (float)M;
+    auto split_q = [&](int q, int &g, int &m) {
+        g = (int)(((float)q + 0.5f) * inv_m);
+        m = q - g * M;
+    };
+    auto stage_pass = [&](int q0, const u32x4 &v) {
+        const int q = q0 + drow;
+        const int e = row16_max(chunk_max_exp(v));
+        const int x = 142 - max(e, 1);
+        const u32x4 h = convert_chunk<4>(v, x);
+        if (q < pairs) {
+            *(u32x4 *)(lds + q * kARowBytes + kc * 16) = h;
+            if (kc == 0) {
+                int g, m;
+                split_q(q, g, m);
+                *(int *)(lds + narrow_exp_offset(G, M) + (g * kTileM + m) * 4) = x;
+            }
+        }
+    };
+    auto load_a = [&](int q0) {
+        int q = q0 + drow;
+        q = q < pairs ? q : pairs - 1;  // clamped: no branch around the load
+        int g, m;
+        split_q(q, g, m);
+        return __builtin_amdgcn_raw_buffer_load_b128(rs.A, (uint32_t)(((int64_t)m * p.K + g * kGroup + kc * 8) * 2), 0, 0);
+    };
+    // exponents of rows M.. are 0 (their activation rows read the zero chunk); zero chunk
+    for (int i = threadIdx.x; i < G * kTileM; i += WAVES * kWave)
+        if (i % kTileM >= M) *(int *)(lds + narrow_exp_offset(G, M) + 4 * i) = 0;
+    if (threadIdx.x == 0) *(u32x4 *)(lds + narrow_zero_offset(G, M)) = u32x4{0u, 0u, 0u, 0u};
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int zero_off = narrow_zero_offset(G, M);
+    const int a_lane = c < M ? c * kARowBytes + kq * 16 : -1;  // -1: a row past M
+    auto compute = [&](int g, const NarrowW &r) {
+        uint32_t magic;
+        asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+        const uint32_t z = r.z & 0xFu;
+        uint32_t zlo = (0xE400u | z) * 0x00010001u, zhi = (0xD400u | (z << 4)) * 0x00010001u;
+        asm volatile("" : "+v"(zlo), "+v"(zhi));
+        const int gbase = g * M * kARowBytes;
+        f32x4 P;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int ao = a_lane >= 0 ? gbase + a_lane + st * 64 : zero_off;
+            const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds + ao));
+            const f16x8 b_op = unpack8(r.w[st], zlo, zhi, magic);
+            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P, 0, 0, 0);
+        }
+        const int4 xr = *(const int4 *)(lds + narrow_exp_offset(G, M) + (g * kTileM + 4 * kq) * 4);
+        const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)r.s);
+        acc[0] = __builtin_fmaf(ldexpf(sv, -xr.x), P[0], acc[0]);
+        acc[1] = __builtin_fmaf(ldexpf(sv, -xr.y), P[1], acc[1]);
+        acc[2] = __builtin_fmaf(ldexpf(sv, -xr.z), P[2], acc[2]);
+        acc[3] = __builtin_fmaf(ldexpf(sv, -xr.w), P[3], acc[3]);
+    };
+
+    // Every weight load of the wave's first kNarrowMaxGroups groups first (the plan keeps a
+    // wave's groups within that), then the activation staging while they are in flight, then
+    // the groups; any further groups are loaded and computed one at a time.
+    auto run = [&](auto kconst) {
+        constexpr int KG = decltype(kconst)::value;
+        NarrowW wr[KG > 0 ? KG : 1];
+        // the first passes' activation loads come before the weights: loads complete in
+        // issue order, so the staging below then overlaps the weight stream
+        constexpr int kPre = 5;
+        u32x4 va[kPre];
+#pragma unroll
+        for (int b = 0; b < kPre; ++b) va[b] = load_a(b * dpp_rows);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < KG; ++u) {
+            load_w(wave + WAVES * u, wr[u]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int b = 0; b < kPre; ++b)
+            if (b * dpp_rows < pairs) stage_pass(b * dpp_rows, va[b]);
+        // any further passes (large M * K): batches of 4, the loads of a batch together
+        for (int q0 = kPre * dpp_rows; q0 < pairs; q0 += 4 * dpp_rows) {
+            u32x4 v[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) v[b] = load_a(q0 + b * dpp_rows);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (q0 + b * dpp_rows < pairs) stage_pass(q0 + b * dpp_rows, v[b]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < KG; ++u) compute(wave + WAVES * u, wr[u]);
+    };
+    switch (n_my) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    case 4: run(std::integral_constant<int, 4>{}); break;
+    case 5: run(std::integral_constant<int, 5>{}); break;
+    case 6: run(std::integral_constant<int, 6>{}); break;
+    case 7: run(std::integral_constant<int, 7>{}); break;
+    default: run(std::integral_constant<int, kNarrowMaxGroups>{}); break;
+    }
+    for (int u = kNarrowMaxGroups; u < n_my; ++u) {
+        NarrowW r;
+        load_w(wave + WAVES * u, r);
+        compute(wave + WAVES * u, r);
+    }
+
+    // Reduce the waves' sums in wave order (reproducible) and write C.
+    __syncthreads();
+    float *red = (float *)lds;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * kq + i;
+        if (row < M) red[(wave * M + row) * kNarrowN + c] = acc[i];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < M * kNarrowN; e += WAVES * kWave) {
+        const int row = e / kNarrowN, col = e % kNarrowN;
+        float sum = red[row * kNarrowN + col];
+        for (int w = 1; w < WAVES; ++w) sum += red[(w * M + row) * kNarrowN + col];
+        if (n0 + col < N) p.C[(int64_t)row * N + n0 + col] = sum;
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -1586,12 +1793,49 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     pl->workspace_bytes = split_tiles * 4 + split_tiles * splits * rows * kTileN * 4;
 }
 
-// Shapes chosen by large_path run on the bf16 matrix-core kernel; everything else on the
-// small-M kernel (row blocks of 16).
+// Narrow-tile kernel: eligible when the rows fit one 16-row block, the staged activations
+// leave room for two workgroups per CU, and no wave holds more than kNarrowMaxGroups
+// groups at once.
+#ifndef W4_NARROW_WAVES
+#define W4_NARROW_WAVES 8
+#endif
+constexpr int kNarrowWaves = W4_NARROW_WAVES;
+constexpr int kNarrowMaxLds = 64 * 1024;
+#ifndef W4_NARROW_RULE
+#define W4_NARROW_RULE 1
+#endif
+
+bool narrow_eligible(int64_t M, int64_t K, int64_t N)
+{
+    const int64_t groups = K / kGroup;
+    const int64_t tiles = (N + kNarrowN - 1) / kNarrowN;
+    return M <= kTileM && groups <= (int64_t)kNarrowMaxGroups * kNarrowWaves &&
+           narrow_lds_bytes((int)groups, (int)M, kNarrowWaves) <= kNarrowMaxLds && tiles <= kCUs;
+}
+
+void make_narrow_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
+{
+    pl->kernel = 8;
+    pl->tile_m = kTileM;
+    pl->tile_n = kNarrowN;
+    pl->m_blocks = 1;
+    pl->n_tiles = (int)((N + kNarrowN - 1) / kNarrowN);
+    pl->splits = 1;
+    pl->groups_per_split = (int)(K / kGroup);
+    pl->full_tiles = 0;
+    pl->workgroups = pl->n_tiles;
+    pl->workspace_bytes = 0;
+}
+
+// Shapes chosen by large_path run on the bf16 matrix-core kernel; narrow outputs whose
+// activations fit in LDS on the narrow-tile kernel; everything else on the small-M kernel
+// (row blocks of 16).
 void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 {
     if (large_path(M, K, N))
         make_large_plan(M, K, N, pl);
+    else if (W4_NARROW_RULE && narrow_eligible(M, K, N))
+        make_narrow_plan(M, K, N, pl);
     else
         make_small_plan(M, K, N, pl);
 }
@@ -1621,6 +1865,7 @@ bool small_instance_exists(int rb, int av, int bits, bool a4)
 bool plan_has_instance(int64_t M, const w4_plan &pl, int bits, bool a4)
 {
     if (pl.kernel == 3) return !a4 && bits == 4 && pl.tile_m >= 1 && pl.tile_m <= kLMaxRT * 32;
+    if (pl.kernel == 8) return !a4 && bits == 4 && M <= kTileM && pl.tile_n == kNarrowN;
     if (pl.tile_m % kTileM != 0) return false;
     const int rows = M < pl.tile_m ? (int)M : pl.tile_m;
     return small_instance_exists(pl.tile_m / kTileM, (rows + 3) / 4, bits, a4);
@@ -1708,7 +1953,21 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         if (st != W4_OK) return st;
     }
     const dim3 grid((unsigned)pl.workgroups);
-    if (pl.kernel == 3) {
+    if (pl.kernel == 8) {
+        NarrowParams q;
+        q.A = (const uint16_t *)A_bf16;
+        q.Wq = Wq;
+        q.S = (const uint16_t *)scales_f16;
+        q.Z = zeros;
+        q.C = C;
+        q.M = M;
+        q.K = K;
+        q.N = N;
+        q.groups = (int)(K / kGroup);
+        q.n_tiles = pl.n_tiles;
+        const size_t lds = (size_t)narrow_lds_bytes(q.groups, (int)M, kNarrowWaves);
+        hipLaunchKernelGGL(w4a16_narrow_kernel<kNarrowWaves>, grid, dim3(kNarrowWaves * kWave), lds, s, q);
+    } else if (pl.kernel == 3) {
         LargeParams q;
         q.A = (const uint16_t *)A_bf16;
         q.Wq = Wq;

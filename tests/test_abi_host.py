@@ -194,9 +194,17 @@ def test_plan_covers_shapes():
             assert p["kernel"] in (4, 5)
         else:
             assert (p["kernel"] == 3) == (M >= 64 or (M >= 17 and K * N >= 1 << 25))
+            # the narrow-tile kernel: rows in one 16-row block, at most 64 groups, staged
+            # activations within 64 KiB, at most one round of 256 tiles
+            G = K // 128
+            stage = max(G * M * 272 + 16 + G * 64, 8 * M * 16 * 4)
+            narrow = M <= 16 and G <= 64 and stage <= 65536 and (N + 15) // 16 <= 256
+            assert (p["kernel"] == 8) == narrow, (M, K, N, p)
         if True:
             if p["kernel"] == 3:
                 assert p["tile_n"] == 256 and p["tile_m"] <= 160
+            elif p["kernel"] == 8:
+                assert (p["tile_m"], p["tile_n"], p["splits"], p["m_blocks"]) == (16, 16, 1, 1)
             else:  # 16-row blocks, or (4-bit activations) one 32-row block at 17..32 rows
                 assert (p["tile_m"], p["tile_n"]) == ((32 if a4 and 16 < M <= 32 else 16), 64)
             assert p["n_tiles"] * p["tile_n"] >= N > (p["n_tiles"] - 1) * p["tile_n"]
@@ -209,9 +217,11 @@ def test_plan_covers_shapes():
             assert full == 0 or (p["kernel"] in (1, 4, 6) and p["splits"] > 1)
             assert p["workgroups"] == full + (tiles - full) * p["splits"]
             assert (p["workspace_bytes"] > 0) == (p["splits"] > 1)
-            if p["kernel"] != 3:  # every workgroup resident at once
+            if p["kernel"] not in (3, 8):  # every workgroup resident at once
                 per_cu = (2 if p["tile_m"] == 32 else 3) if p["kernel"] in (1, 4, 6) else 1
                 assert p["workgroups"] <= 256 * per_cu or p["splits"] == 1
+            if p["kernel"] == 8:
+                assert p["workgroups"] == p["n_tiles"] <= 256
     with pytest.raises(w4.W4Error):
         w4.plan(5, 100, 64)
 
@@ -240,9 +250,13 @@ def test_measured_plan_choices():
     # qkv and o at M=5 take the wide shape at 3 splits (a tall workgroup would leave waves
     # idle), down keeps the tall shape at 4 splits, and 8-bit down at M=1 spreads over 96 CUs
     # with the wide shape (8-bit near-ties at M <= 4: 9.41 us tall, 8.60 wide)
-    for K, N in ((3584, 4608), (3584, 3584)):
-        p = w4.plan(5, K, N)
-        assert (p["kernel"], p["splits"]) == (1, 3), (K, N, p)
+    p = w4.plan(5, 3584, 4608)
+    assert (p["kernel"], p["splits"]) == (1, 3), p
+    # o at M=5 (224 sixteen-column tiles, one round of CUs) runs on the narrow-tile kernel
+    # without a K split: 7.20 -> 5.48 us measured (graph replays, weights from HBM); qkv
+    # (288 tiles, a second partial round) measured 7.46 small-M against 8.52 narrow
+    p = w4.plan(5, 3584, 3584)
+    assert (p["kernel"], p["splits"], p["workgroups"]) == (8, 1, 224), p
     p = w4.plan(5, 18944, 3584)
     assert (p["kernel"], p["splits"]) == (2, 4), p
     p = w4.plan(1, 8960, 1536, bits=8)
@@ -262,7 +276,9 @@ def test_measured_plan_choices():
     # a single 16-row block hands a tall plan at one group per wave to the wide shape (M=1
     # draft: qkv 4.52 -> 4.49, o 4.70 -> 4.57, down 7.36 -> 7.16 us; 8-bit qkv 5.69 -> 5.36 us);
     # more rows per workgroup keep the tall shape (W4A4 at M=32: 9.21 tall, 10.30 wide)
-    for K, N, want in ((1536, 2048, (1, 1)), (1536, 1536, (1, 1)), (8960, 1536, (1, 6))):
+    # the M=1 draft's qkv and o run narrow (4.56 -> 3.52 and 4.55 -> 3.48 us); its down
+    # (70 groups, more than a wave's eight at once) keeps the small-M split plan
+    for K, N, want in ((1536, 2048, (8, 1)), (1536, 1536, (8, 1)), (8960, 1536, (1, 6))):
         p = w4.plan(1, K, N)
         assert (p["kernel"], p["splits"]) == want, (K, N, p)
     for K, N in ((1536, 2048), (1536, 1536)):

@@ -241,6 +241,47 @@ def test_maximum_sizes(orc, M, K, N):
     check(C[np.ix_(rows, cols)], Cr, Cabs, f"max size M={M} K={K} N={N}")
 
 
+# ------------------------------------------------------------- narrow-tile kernel
+NARROW_SHAPES = [(1, 8192, 4095), (5, 3584, 3584), (8, 3584, 1000), (16, 1792, 300), (3, 128, 17),
+                 (7, 640, 4096), (2, 8064, 33), (4, 1024, 1), (6, 2304, 257), (1, 1536, 2048)]
+
+
+@pytest.mark.parametrize("M,K,N", NARROW_SHAPES)
+def test_narrow_kernel_every_element(orc, M, K, N):
+    # one 16-column tile per workgroup over all of K: 64 groups (eight per wave, the most a
+    # wave holds), one group (seven idle waves), ragged N down to a single column, 16 rows,
+    # 256 tiles; NaN-poisoned C, every element against the oracle
+    p = w4.plan(M, K, N)
+    log(f"narrow M={M} K={K} N={N} plan={p}")
+    assert p["kernel"] == 8 and p["tile_n"] == 16 and p["splits"] == 1
+    x = synth.generate_custom(M, K, N, seed=61)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    C = run(to_dev(x), out=out).cpu().numpy()
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
+    check(C, Cr, Cabs, f"narrow M={M} K={K} N={N}")
+
+
+def test_narrow_kernel_one_hot_and_zero_bitwise(orc):
+    # exact special cases on the narrow kernel: one-hot rows extract one dequantized row bit
+    # for bit, and q == z gives exact zeros
+    M, K, N = 5, 2048, 200
+    assert w4.plan(M, K, N)["kernel"] == 8
+    x = synth.generate_custom(M, K, N, seed=62)
+    dev = to_dev(x)
+    for (m0, k0, a0) in ((0, 0, 1.0), (M - 1, K - 1, -2.5), (2, 1037, 3.0e4), (3, 128, -0.0078125)):
+        A = np.zeros((M, K), np.float32)
+        A[m0, k0] = a0
+        Ab = synth.f32_to_bf16_bits(A)
+        dev["A"] = torch.from_numpy(Ab.view(np.int16)).cuda().view(torch.bfloat16)
+        log(f"narrow one-hot m={m0} k={k0} a={a0}")
+        C = run(dev).cpu().numpy().astype(np.float64)
+        Cr, _ = orc.gemm(Ab, x.Wq, x.S, x.Z)
+        assert np.array_equal(C, Cr), f"one-hot ({m0},{k0}) differs"
+    q = np.repeat(x.Z, 128, axis=0).astype(np.uint8)
+    C = run(to_dev(synth.GemmInputs(A=x.A, Wq=orc.pack(q), q=None, S=x.S, Z=x.Z))).cpu().numpy()
+    assert np.all(C == 0.0)
+
+
 # ----------------------------------------------------------------- exact special cases
 @pytest.mark.parametrize("M,K,N", [(5, 384, 72), (16, 1152, 64), (1, 4096, 33)])
 def test_one_hot_bitwise(orc, M, K, N):
