@@ -35,6 +35,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <type_traits>
@@ -1796,14 +1797,10 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
 // Narrow-tile kernel: eligible when the rows fit one 16-row block, the staged activations
 // leave room for two workgroups per CU, and no wave holds more than kNarrowMaxGroups
 // groups at once.
-#ifndef W4_NARROW_WAVES
-#define W4_NARROW_WAVES 8
-#endif
-constexpr int kNarrowWaves = W4_NARROW_WAVES;
+// (8 waves measured fastest: 12 and 16 waves per workgroup were 2-30% slower on every
+// planned shape.)
+constexpr int kNarrowWaves = 8;
 constexpr int kNarrowMaxLds = 64 * 1024;
-#ifndef W4_NARROW_RULE
-#define W4_NARROW_RULE 1
-#endif
 
 bool narrow_eligible(int64_t M, int64_t K, int64_t N)
 {
@@ -1834,7 +1831,7 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 {
     if (large_path(M, K, N))
         make_large_plan(M, K, N, pl);
-    else if (W4_NARROW_RULE && narrow_eligible(M, K, N))
+    else if (narrow_eligible(M, K, N))
         make_narrow_plan(M, K, N, pl);
     else
         make_small_plan(M, K, N, pl);
