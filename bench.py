@@ -39,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(ROOT, "int4_weight_only_gemm_amd", "csrc", "w4a16.hip")
 KERNEL_NAME = "w4a16_kernel"           # small M: fp16 matrix cores, exact (q - z) operands
 KERNEL_NAME_LARGE = "w4a16_mfma_kernel"  # M >= 64 (and large GEMMs from M = 17): bf16 matrix cores
+KERNEL_NAME_NARROW = "w4a16_narrow_kernel"  # M <= 16, few tiles: one 16-column tile over all of K
 # HBM bytes per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE passes (a text summary with
 # "key: value" lines); used only while the kernel source hash and workload still match.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_w4a16_kernel_qwen2.5-7b-verify-m5.md")
@@ -296,14 +297,20 @@ def main():
     # Roofline figures of the dominant kernel.  The bound follows the step's arithmetic
     # intensity against the ridge of the two peaks (2*M flops per 0.5234375 weight bytes:
     # matrix-core-bound from M ~ 82 on); the named kernel is the one streaming most of the
-    # step's weight bytes.  Its average launch duration is the timed region (HIP events on
-    # the launch stream) divided by the launches it holds, and the algorithmic bytes (or
-    # flops) per launch are the step's totals divided by the same count.
+    # step's weight bytes, and every GEMM kernel of the step is listed with its share of
+    # those bytes.  The average launch duration is the timed region (HIP events on the launch
+    # stream) divided by the GEMM launches it holds, so it covers all of the step's GEMM
+    # kernels; the algorithmic bytes (or flops) per launch are the step's totals divided by
+    # the same count.
     launches = args.steps * len(calls)
     avg_dur_s = elapsed_ms * 1e-3 / launches
     kinds = [w4.plan(spec.M, spec.K, spec.N, bits=spec.bits, a4=spec.act4)["kernel"] for spec, _ in gemms]
-    large_bytes = sum(spec.weight_bytes for (spec, _), k in zip(gemms, kinds) if k == 3)
-    kernel = KERNEL_NAME_LARGE if 2 * large_bytes > wl.weight_bytes else KERNEL_NAME
+    share = {}
+    for (spec, _), k in zip(gemms, kinds):
+        name = KERNEL_NAME_LARGE if k == 3 else (KERNEL_NAME_NARROW if k == 8 else KERNEL_NAME)
+        share[name] = share.get(name, 0) + spec.weight_bytes
+    kernel = max(share, key=share.get)
+    share = {name: round(b / wl.weight_bytes, 4) for name, b in share.items()}
     dtype = "bf16" if all(k == 3 for k in kinds) else ("f16" if all(k != 3 for k in kinds) else "f16+bf16")
     mfma_bound = wl.flops / wl.weight_bytes > MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:  # a dense contraction, priced against the bf16 MFMA peak
@@ -434,6 +441,7 @@ def main():
         "roofline": {
             "bound": bound,
             "kernel": kernel,
+            "weight_byte_share": share,
             "achieved": round(achieved, 2),
             "peak": peak,
             "unit": unit,
