@@ -485,7 +485,8 @@ void w4a16_kernel(SmallParams p)
     // their loads are served first, so the parts and their handoff finish while the whole
     // tiles still stream (dispatched last, the parts were the last workgroups to finish:
     // 3584x37888 at M = 5 measured 18.24 -> 17.89 us, 1536x17920 at M = 1 7.39 -> 6.24 us).
-    // Each range spreads evenly over the XCDs (and over the CUs of an XCD).
+    // The parts' range starts at workgroup 0, so the splits of one tile run on one XCD; the
+    // whole tiles (independent of each other) follow, spread over the XCDs.
     const uint32_t nfull = (uint32_t)p.full_tiles;
     const uint32_t nparts = gridDim.x - nfull;
     uint32_t tile;
