@@ -508,6 +508,11 @@ void w4a16_kernel(SmallParams p)
     constexpr int kExpOffset = pipe_exp_offset(RB);
     extern __shared__ __attribute__((aligned(16))) char lds[];  // per-wave tiles, then reduction
     __shared__ int s_last;
+    // every kernel argument is fetched at entry, in one round trip: left to the compiler, the
+    // pointers come in a second scalar load after the tile mapping's branches
+    asm volatile("" ::"s"(p.A), "s"(p.Wq), "s"(p.S), "s"(p.Z), "s"(p.C), "s"(p.part), "s"(p.count), "s"(p.M),
+                 "s"(p.K), "s"(p.N), "s"(p.groups), "s"(p.splits), "s"(p.gps), "s"(p.n_tiles), "s"(p.m_blocks),
+                 "s"(p.full_tiles), "s"(gridDim.x));
 
     // Tiles [0, full_tiles) run unsplit, one workgroup each; the other tiles are split
     // `splits` ways, and their parts are dispatched first: issued ahead of the whole tiles,
@@ -797,6 +802,9 @@ template <int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(NarrowParams p)
 {
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    // all kernel arguments in one scalar round trip at entry (see w4a16_kernel)
+    asm volatile("" ::"s"(p.A), "s"(p.Wq), "s"(p.S), "s"(p.Z), "s"(p.C), "s"(p.M), "s"(p.K), "s"(p.N),
+                 "s"(p.groups), "s"(gridDim.x));
     const int tile = (int)xcd_local_id(blockIdx.x, gridDim.x);
     const int n0 = tile * kNarrowN;
     const int M = (int)p.M, G = p.groups;
@@ -1036,6 +1044,12 @@ void w4a16_mfma_kernel(LargeParams p)
     static_assert(kRows * kChunksPerRow % kLThreads == 0, "staging must tile the block");
     constexpr int kSteps = RT * 8;  // MFMAs per group per wave
     __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
+    // all kernel arguments in one scalar round trip at entry (see w4a16_kernel); at five row
+    // tiles the second round trip is already hidden and forcing the first measured slower
+    if constexpr (RT < 5)
+        asm volatile("" ::"s"(p.A), "s"(p.Wq), "s"(p.S), "s"(p.Z), "s"(p.C), "s"(p.part), "s"(p.stride),
+                     "s"(p.M), "s"(p.K), "s"(p.N), "s"(p.groups), "s"(p.splits), "s"(p.gps), "s"(p.n_tiles),
+                     "s"(p.block_rows));
 
     const uint32_t logical = blockIdx.x;
     const int sp = (int)(logical % (uint32_t)p.splits);
