@@ -1027,6 +1027,45 @@ __device__ __forceinline__ bf16x8 unpack8_bf16(uint32_t w, uint32_t zz)
     return __builtin_bit_cast(bf16x8, r);
 }
 
+// unpack8_bf16 in five pieces of 3-4 VALU operations each, so that a word's dequantization
+// can be spread over five matrix-core steps (piece 4 completes r).  Interleaved this way the
+// VALU work overlaps the matrix cores far better than in bursts of ~19 operations.
+struct Unpack8 {
+    uint32_t ev, od, t;
+    float d0;
+    u32x4 r;
+};
+// Each piece's results are pinned where the piece stands: without that, the compiler sinks
+// the arithmetic to the first use and the pieces bunch up again.
+__device__ __forceinline__ void unpack8_piece(int piece, Unpack8 &u, uint32_t w, uint32_t zz)
+{
+    switch (piece) {
+    case 0:
+        u.ev = (((w & 0x0F0F0F0Fu) | 0x80808080u) - zz) ^ 0x80808080u;  // q0 q2 q4 q6
+        u.t = w >> 4;
+        asm volatile("" : "+v"(u.ev), "+v"(u.t));
+        break;
+    case 1:
+        u.od = (((u.t & 0x0F0F0F0Fu) | 0x80808080u) - zz) ^ 0x80808080u;  // q1 q3 q5 q7
+        u.d0 = (float)(int8_t)u.ev;
+        asm volatile("" : "+v"(u.od), "+v"(u.d0));
+        break;
+    case 2:
+        u.r[0] = pack_bf2(u.d0, (float)(int8_t)u.od);
+        u.r[1] = pack_bf2((float)(int8_t)(u.ev >> 8), (float)(int8_t)(u.od >> 8));
+        asm volatile("" : "+v"(u.r[0]), "+v"(u.r[1]));
+        break;
+    case 3:
+        u.r[2] = pack_bf2((float)(int8_t)(u.ev >> 16), (float)(int8_t)(u.od >> 16));
+        asm volatile("" : "+v"(u.r[2]));
+        break;
+    default:
+        u.r[3] = pack_bf2((float)(int8_t)(u.ev >> 24), (float)(int8_t)(u.od >> 24));
+        asm volatile("" : "+v"(u.r[3]));
+        break;
+    }
+}
+
 // One group's packed words for the lane's column: word ks holds k = 16 ks + 8 h .. + 7.
 struct LargeW {
     uint32_t w[8];
@@ -1146,10 +1185,12 @@ void w4a16_mfma_kernel(LargeParams p)
         auto a_at = [&](int step) { return *(const bf16x8 *)(abase + (step >> 3) * 32 * kARowBytes + (step & 7) * 32); };
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) ring[i] = a_at(i);
-        // Step (rt, ks): read the A operand two steps ahead, issue the MFMA, then a share
-        // of the VALU work: dequantize one word every RT steps, and rescale two of row tile
-        // rt - 1's sixteen partials (their MFMAs finished a row tile ago).  A scheduling
-        // barrier after each step keeps this order.
+        // Step (rt, ks): read the A operand two steps ahead, issue the MFMA, then an even
+        // share of the VALU work, a few operations per MFMA: word step / RT's dequantization
+        // in pieces over RT steps, and from ks = 1 on the rescale of row tile rt - 1, whose
+        // last MFMA issued a step earlier.  A scheduling barrier after each step keeps this
+        // order.
+        Unpack8 u;
         f32x16 P, Q;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -1164,10 +1205,16 @@ void w4a16_mfma_kernel(LargeParams p)
                 } else {
                     P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], P, 0, 0, 0);
                 }
-                if (step % RT == 0) Bn[step / RT] = unpack8_bf16(Wn.w[step / RT], zzn);
-                if (rt > 0) {
-                    acc[rt - 1][2 * ks] = __builtin_fmaf(sc, Q[2 * ks], acc[rt - 1][2 * ks]);
-                    acc[rt - 1][2 * ks + 1] = __builtin_fmaf(sc, Q[2 * ks + 1], acc[rt - 1][2 * ks + 1]);
+                const int word = step / RT, l = step % RT;
+#pragma unroll
+                for (int pc = l * 5 / RT; pc < (l + 1) * 5 / RT; ++pc) unpack8_piece(pc, u, Wn.w[word], zzn);
+                if (l == RT - 1) Bn[word] = __builtin_bit_cast(bf16x8, u.r);
+                // rescale of 16 partials over ks = 1..7: 2, 2, 2, 2, 2, 3, 3
+                if (rt > 0 && ks > 0) {
+                    const int v0 = ks <= 5 ? 2 * (ks - 1) : 10 + 3 * (ks - 6);
+                    const int nv = ks <= 5 ? 2 : 3;
+#pragma unroll
+                    for (int v = v0; v < v0 + nv; ++v) acc[rt - 1][v] = __builtin_fmaf(sc, Q[v], acc[rt - 1][v]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
