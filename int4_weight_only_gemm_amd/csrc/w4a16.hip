@@ -509,10 +509,12 @@ void w4a16_kernel(SmallParams p)
     extern __shared__ __attribute__((aligned(16))) char lds[];  // per-wave tiles, then reduction
     __shared__ int s_last;
     // every kernel argument is fetched at entry, in one round trip: left to the compiler, the
-    // pointers come in a second scalar load after the tile mapping's branches
+    // pointers come in a second scalar load after the tile mapping's branches (4-bit
+    // activations add their scale pointer)
     asm volatile("" ::"s"(p.A), "s"(p.Wq), "s"(p.S), "s"(p.Z), "s"(p.C), "s"(p.part), "s"(p.count), "s"(p.M),
                  "s"(p.K), "s"(p.N), "s"(p.groups), "s"(p.splits), "s"(p.gps), "s"(p.n_tiles), "s"(p.m_blocks),
-                 "s"(p.full_tiles), "s"(gridDim.x));
+                 "s"(p.full_tiles));
+    if constexpr (A4) asm volatile("" ::"s"(p.As));
 
     // Tiles [0, full_tiles) run unsplit, one workgroup each; the other tiles are split
     // `splits` ways, and their parts are dispatched first: issued ahead of the whole tiles,
@@ -522,7 +524,9 @@ void w4a16_kernel(SmallParams p)
     // The parts' range starts at workgroup 0, so the splits of one tile run on one XCD; the
     // whole tiles (independent of each other) follow, spread over the XCDs.
     const uint32_t nfull = (uint32_t)p.full_tiles;
-    const uint32_t nparts = gridDim.x - nfull;
+    // the grid is nfull + nparts workgroups (computed here rather than read from the grid
+    // size, a hidden argument the compiler fetches in a round trip of its own)
+    const uint32_t nparts = ((uint32_t)p.m_blocks * (uint32_t)p.n_tiles - nfull) * (uint32_t)p.splits;
     uint32_t tile;
     int sp, gps;
     if (blockIdx.x >= nparts) {
@@ -2159,6 +2163,12 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         p.n_tiles = pl.n_tiles;
         p.m_blocks = pl.m_blocks;
         p.full_tiles = pl.full_tiles;
+        // the kernel derives its split-part count from these fields instead of the grid size
+        if (pl.workgroups != (int64_t)pl.full_tiles + ((int64_t)pl.m_blocks * pl.n_tiles - pl.full_tiles) * pl.splits) {
+            set_error("w4a16_gemm: internal error: plan grid (%lld workgroups) does not match its tiles",
+                      (long long)pl.workgroups);
+            return W4_ERR_PLAN;
+        }
         const bool vec = (N % 4 == 0) && aligned(scales_f16, 8) && aligned(zeros, 4);
         const size_t lds = plan_lds_bytes(M, pl);
         const int rb = pl.tile_m / kTileM;
