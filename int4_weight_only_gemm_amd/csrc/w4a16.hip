@@ -1070,6 +1070,34 @@ __device__ __forceinline__ void unpack8_piece(int piece, Unpack8 &u, uint32_t w,
     }
 }
 
+// Order of a large-M workgroup's RT * 8 MFMA steps per group: row tiles in segments of one
+// or two (RT = 2: {0,1}; 3: {0} {1,2}; 4: {0,1} {2,3}; 1 and 5: one tile per segment, five
+// need the registers a second chain would take); within a segment of two the tiles
+// alternate per k-step.
+template <int RT> __host__ __device__ constexpr int large_segments() { return RT == 2 ? 1 : RT == 3 || RT == 4 ? 2 : RT; }
+template <int RT> __host__ __device__ constexpr int large_seg_first(int sg)
+{
+    return RT == 2 ? 0 : RT == 3 ? (sg == 0 ? 0 : 1) : RT == 4 ? 2 * sg : sg;
+}
+template <int RT> __host__ __device__ constexpr int large_seg_count(int sg)
+{
+    return RT == 2 ? 2 : RT == 3 ? (sg == 0 ? 1 : 2) : RT == 4 ? 2 : 1;
+}
+template <int RT> __host__ __device__ constexpr int large_step_rt(int n)
+{
+    if (RT == 2) return n & 1;
+    if (RT == 3) return n < 8 ? 0 : 1 + ((n - 8) & 1);
+    if (RT == 4) return 2 * (n / 16) + (n & 1);
+    return n >> 3;
+}
+template <int RT> __host__ __device__ constexpr int large_step_ks(int n)
+{
+    if (RT == 2) return n >> 1;
+    if (RT == 3) return n < 8 ? n : (n - 8) >> 1;
+    if (RT == 4) return (n % 16) >> 1;
+    return n & 7;
+}
+
 // One group's packed words for the lane's column: word ks holds k = 16 ks + 8 h .. + 7.
 struct LargeW {
     uint32_t w[8];
@@ -1184,48 +1212,63 @@ void w4a16_mfma_kernel(LargeParams p)
 
         const char *abase = lds + buf * kBuf + a_lane;
         const uint32_t zzn = (Wn.z & 0xFu) * 0x01010101u;
-        constexpr int kAhead = 2;  // A operands read two steps ahead (step = rt * 8 + ks)
+        constexpr int kAhead = 2;  // A operands read two MFMA steps ahead
         bf16x8 ring[kAhead + 1];
-        auto a_at = [&](int step) { return *(const bf16x8 *)(abase + (step >> 3) * 32 * kARowBytes + (step & 7) * 32); };
+        auto a_at = [&](int n) {
+            return *(const bf16x8 *)(abase + large_step_rt<RT>(n) * 32 * kARowBytes + large_step_ks<RT>(n) * 32);
+        };
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) ring[i] = a_at(i);
-        // Step (rt, ks): read the A operand two steps ahead, issue the MFMA, then an even
-        // share of the VALU work, a few operations per MFMA: word step / RT's dequantization
-        // in pieces over RT steps, and from ks = 1 on the rescale of row tile rt - 1, whose
-        // last MFMA issued a step earlier.  A scheduling barrier after each step keeps this
-        // order.
+        // MFMA step n runs (row tile, k-step) = (large_step_rt, large_step_ks): the row tiles
+        // go in segments of one or two, and a segment of two interleaves its tiles' chains
+        // per k-step (two independent accumulation chains hide each other's MFMA latency).
+        // After each MFMA an even share of the VALU work: word n / RT's dequantization in
+        // pieces over RT steps, and, from the segment's second step on, the rescale of the
+        // previous segment's row tiles.  A scheduling barrier after each step keeps this
+        // order.  Row tile rt accumulates in chain rt % 2 and is rescaled from Q[rt % 2].
         Unpack8 u;
-        f32x16 P, Q;
+        f32x16 P[2], Q[2];
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
+        for (int sg = 0; sg < large_segments<RT>(); ++sg) {
+            const int r0 = large_seg_first<RT>(sg), cnt = large_seg_count<RT>(sg);
+            const int base = 8 * r0, len = 8 * cnt;
+            const int pr0 = sg > 0 ? large_seg_first<RT>(sg - 1) : 0;
+            const int pending = sg > 0 ? 16 * large_seg_count<RT>(sg - 1) : 0;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int step = rt * 8 + ks;
-                if (step + kAhead < kSteps) ring[(step + kAhead) % (kAhead + 1)] = a_at(step + kAhead);
-                const bf16x8 a = ring[step % (kAhead + 1)];
+            for (int i = 0; i < len; ++i) {
+                const int n = base + i;
+                const int rt = large_step_rt<RT>(n), ks = large_step_ks<RT>(n);
+                if (n + kAhead < kSteps) ring[(n + kAhead) % (kAhead + 1)] = a_at(n + kAhead);
+                const bf16x8 a = ring[n % (kAhead + 1)];
+                f32x16 &Pc = P[rt & 1];
                 if (ks == 0) {
                     const f32x16 zero = {};
-                    P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], zero, 0, 0, 0);
+                    Pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], zero, 0, 0, 0);
                 } else {
-                    P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], P, 0, 0, 0);
+                    Pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], Pc, 0, 0, 0);
                 }
-                const int word = step / RT, l = step % RT;
+                const int word = n / RT, l = n % RT;
 #pragma unroll
                 for (int pc = l * 5 / RT; pc < (l + 1) * 5 / RT; ++pc) unpack8_piece(pc, u, Wn.w[word], zzn);
                 if (l == RT - 1) Bn[word] = __builtin_bit_cast(bf16x8, u.r);
-                // rescale of 16 partials over ks = 1..7: 2, 2, 2, 2, 2, 3, 3
-                if (rt > 0 && ks > 0) {
-                    const int v0 = ks <= 5 ? 2 * (ks - 1) : 10 + 3 * (ks - 6);
-                    const int nv = ks <= 5 ? 2 : 3;
+                // the previous segment's partials, spread over steps 1 .. len - 1
+                if (pending > 0 && i > 0) {
+                    const int f0 = (i - 1) * pending / (len - 1), f1 = i * pending / (len - 1);
 #pragma unroll
-                    for (int v = v0; v < v0 + nv; ++v) acc[rt - 1][v] = __builtin_fmaf(sc, Q[v], acc[rt - 1][v]);
+                    for (int f = f0; f < f1; ++f) {
+                        const int tr = pr0 + f / 16, v = f % 16;
+                        acc[tr][v] = __builtin_fmaf(sc, Q[tr & 1][v], acc[tr][v]);
+                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            Q = P;
-            // stage one chunk of the next group's activations per row tile, so the LDS
-            // writes spread over the group instead of queueing behind its reads at the end
-            *(u32x4 *)(lds + (buf ^ 1) * kBuf + alds[rt]) = ar[rt];
+#pragma unroll
+            for (int c = 0; c < cnt; ++c) {
+                Q[(r0 + c) & 1] = P[(r0 + c) & 1];
+                // stage one chunk of the next group's activations per row tile, so the LDS
+                // writes spread over the group instead of queueing behind its reads at the end
+                *(u32x4 *)(lds + (buf ^ 1) * kBuf + alds[r0 + c]) = ar[r0 + c];
+            }
         }
         scn = scale_of(Wn);
         // ... and keep it from sinking into the next group: the operands are complete here.
@@ -1234,8 +1277,15 @@ void w4a16_mfma_kernel(LargeParams p)
         // The barrier comes as soon as this wave's LDS traffic for the group is done; the
         // last row tile's rescale (which waits for its MFMAs) follows it.
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        {
+            constexpr int last = large_segments<RT>() - 1;
+            const int r0 = large_seg_first<RT>(last), cnt = large_seg_count<RT>(last);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[RT - 1][v] = __builtin_fmaf(sc, Q[v], acc[RT - 1][v]);
+            for (int c = 0; c < cnt; ++c)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[r0 + c][v] = __builtin_fmaf(sc, Q[(r0 + c) & 1][v], acc[r0 + c][v]);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -2165,7 +2215,7 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         p.full_tiles = pl.full_tiles;
         // the kernel derives its split-part count from these fields instead of the grid size
         if (pl.workgroups != (int64_t)pl.full_tiles + ((int64_t)pl.m_blocks * pl.n_tiles - pl.full_tiles) * pl.splits) {
-            set_error("w4a16_gemm: internal error: plan grid (%lld workgroups) does not match its tiles",
+            set_error("%s: internal error: plan grid (%lld workgroups) does not match its tiles", name,
                       (long long)pl.workgroups);
             return W4_ERR_PLAN;
         }
