@@ -17,6 +17,10 @@ FLAGS = [
     "-Wall", "-Wno-unused-function",
     # packed fp32 VALU ops stay off on this target
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 14 dwords of each kernel's arguments are preloaded into scalar registers at
+    # wave launch (the kernels put what they need before their first load there); code
+    # objects keep a scalar-load prologue for firmware without preload
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
 ]
 
 

@@ -98,6 +98,17 @@ struct SmallParams {
     const float *As;    // 4-bit activations only: float32 scales [M, K/128]
 };
 
+// The small-M kernel's arguments: the fields every wave needs before its first weight load
+// come first, 14 dwords in all, which is what the hardware can preload into scalar registers
+// at wave launch (the tile and row-block counts follow from N and M); the rest follows as a
+// struct.
+struct SmallTail {
+    float *C;
+    float *part;
+    unsigned *count;
+    const float *As;
+};
+
 // ------------------------------------------------------------------------------------
 // Bit-level helpers
 
@@ -502,19 +513,32 @@ __device__ __forceinline__ void compute_pipe(const GroupRegs<BITS> &r, const cha
 
 template <bool VEC, int WAVES, int AV, int OCC, int BITS, bool A4, int RB, bool T1>
 __global__ __launch_bounds__(WAVES * kWave) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
-void w4a16_kernel(SmallParams p)
+void w4a16_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S, const uint8_t *Z, int M, int K, int N,
+                  int splits, int groups_per_split, int full_tiles, SmallTail tail)
 {
     constexpr int kRows = RB * kTileM;  // rows per block: one or two matrix-core row tiles
     constexpr int kExpOffset = pipe_exp_offset(RB);
     extern __shared__ __attribute__((aligned(16))) char lds[];  // per-wave tiles, then reduction
     __shared__ int s_last;
-    // every kernel argument is fetched at entry, in one round trip: left to the compiler, the
-    // pointers come in a second scalar load after the tile mapping's branches (4-bit
-    // activations add their scale pointer)
-    asm volatile("" ::"s"(p.A), "s"(p.Wq), "s"(p.S), "s"(p.Z), "s"(p.C), "s"(p.part), "s"(p.count), "s"(p.M),
-                 "s"(p.K), "s"(p.N), "s"(p.groups), "s"(p.splits), "s"(p.gps), "s"(p.n_tiles), "s"(p.m_blocks),
-                 "s"(p.full_tiles));
-    if constexpr (A4) asm volatile("" ::"s"(p.As));
+    SmallParams p;
+    p.A = A;
+    p.Wq = Wq;
+    p.S = S;
+    p.Z = Z;
+    p.C = tail.C;
+    p.part = tail.part;
+    p.count = tail.count;
+    p.As = tail.As;
+    p.M = M;
+    p.K = K;
+    p.N = N;
+    p.groups = K / kGroup;
+    p.splits = splits;
+    p.gps = groups_per_split;
+    p.n_tiles = (N + kTileN - 1) / kTileN;
+    p.m_blocks = (M + kRows - 1) / kRows;
+    p.full_tiles = full_tiles;
+    if constexpr (A4) asm volatile("" ::"s"(p.As));  // the one pointer needed early that is not preloaded
 
     // Tiles [0, full_tiles) run unsplit, one workgroup each; the other tiles are split
     // `splits` ways, and their parts are dispatched first: issued ahead of the whole tiles,
@@ -803,13 +827,25 @@ struct NarrowW {
 };
 
 template <int WAVES>
-__global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(NarrowParams p)
+__global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(const uint16_t *A, const uint32_t *Wq,
+                                                                      const uint16_t *S, const uint8_t *Z, float *C,
+                                                                      int M_, int K_, int N_, int groups)
 {
+    // 14 dwords of arguments, all preloaded into scalar registers at wave launch; the grid
+    // (one workgroup per tile) is derived from N rather than read from a hidden argument
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    // all kernel arguments in one scalar round trip at entry (see w4a16_kernel)
-    asm volatile("" ::"s"(p.A), "s"(p.Wq), "s"(p.S), "s"(p.Z), "s"(p.C), "s"(p.M), "s"(p.K), "s"(p.N),
-                 "s"(p.groups), "s"(gridDim.x));
-    const int tile = (int)xcd_local_id(blockIdx.x, gridDim.x);
+    NarrowParams p;
+    p.A = A;
+    p.Wq = Wq;
+    p.S = S;
+    p.Z = Z;
+    p.C = C;
+    p.M = M_;
+    p.K = K_;
+    p.N = N_;
+    p.groups = groups;
+    p.n_tiles = (N_ + kNarrowN - 1) / kNarrowN;
+    const int tile = (int)xcd_local_id(blockIdx.x, (uint32_t)p.n_tiles);
     const int n0 = tile * kNarrowN;
     const int M = (int)p.M, G = p.groups;
     const int lane = threadIdx.x & 63;
@@ -1011,6 +1047,15 @@ struct LargeParams {
     int block_rows;     // rows per row block (<= RT * 32)
 };
 
+// The large-M kernel's arguments: the 14 dwords every wave needs before its first load
+// (preloaded into scalar registers at wave launch; the tile count follows from N), then the
+// output side as a struct.
+struct LargeTail {
+    float *C;
+    float *part;
+    int64_t stride;
+};
+
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b)
 {
     bf16x2 h = {(__bf16)a, (__bf16)b};
@@ -1107,7 +1152,8 @@ struct LargeW {
 
 template <int RT>
 __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void w4a16_mfma_kernel(LargeParams p)
+void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S, const uint8_t *Z, int M_, int K_,
+                       int N_, int groups_per_split, int splits, int block_rows, LargeTail tail)
 {
     constexpr int kRows = RT * 32;
     constexpr int kBuf = kRows * kARowBytes;
@@ -1115,12 +1161,23 @@ void w4a16_mfma_kernel(LargeParams p)
     static_assert(kRows * kChunksPerRow % kLThreads == 0, "staging must tile the block");
     constexpr int kSteps = RT * 8;  // MFMAs per group per wave
     __shared__ __attribute__((aligned(16))) char lds[2 * kBuf];
-    // all kernel arguments in one scalar round trip at entry (see w4a16_kernel); at five row
-    // tiles the second round trip is already hidden and forcing the first measured slower
-    if constexpr (RT < 5)
-        asm volatile("" ::"s"(p.A), "s"(p.Wq), "s"(p.S), "s"(p.Z), "s"(p.C), "s"(p.part), "s"(p.stride),
-                     "s"(p.M), "s"(p.K), "s"(p.N), "s"(p.groups), "s"(p.splits), "s"(p.gps), "s"(p.n_tiles),
-                     "s"(p.block_rows));
+    LargeParams p;
+    p.A = A;
+    p.Wq = Wq;
+    p.S = S;
+    p.Z = Z;
+    p.C = tail.C;
+    p.part = tail.part;
+    p.stride = tail.stride;
+    p.M = M_;
+    p.K = K_;
+    p.N = N_;
+    p.groups = K_ / kGroup;
+    p.splits = splits;
+    p.gps = groups_per_split;
+    p.n_tiles = (N_ + kLTileN - 1) / kLTileN;
+    p.m_blocks = 0;  // not used by the kernel
+    p.block_rows = block_rows;
 
     const uint32_t logical = blockIdx.x;
     const int sp = (int)(logical % (uint32_t)p.splits);
@@ -2059,10 +2116,12 @@ template <int BITS, bool A4>
 bool launch_small(bool tall, int rb, int av, bool vec, bool t1, dim3 grid, size_t lds, hipStream_t s,
                   const SmallParams &p)
 {
+    const SmallTail tail = {p.C, p.part, p.count, p.As};
+#define W4_ARGS p.A, p.Wq, p.S, p.Z, (int)p.M, (int)p.K, (int)p.N, p.splits, p.gps, p.full_tiles, tail
 #define W4_LAUNCH(V, WV, AVV, OCCV, RBV) \
-    hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, OCCV, BITS, A4, RBV, false>), grid, dim3(WV * kWave), lds, s, p)
+    hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, OCCV, BITS, A4, RBV, false>), grid, dim3(WV * kWave), lds, s, W4_ARGS)
 #define W4_LAUNCH_T1(V, WV, AVV) \
-    hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, kOccupancy, BITS, A4, 1, true>), grid, dim3(WV * kWave), lds, s, p)
+    hipLaunchKernelGGL((w4a16_kernel<V, WV, AVV, kOccupancy, BITS, A4, 1, true>), grid, dim3(WV * kWave), lds, s, W4_ARGS)
 #define W4_LAUNCH_16T1(V, WV) \
     switch (av) { case 2: W4_LAUNCH_T1(V, WV, 2); break; case 3: W4_LAUNCH_T1(V, WV, 3); break; \
                   default: W4_LAUNCH_T1(V, WV, 4); break; }
@@ -2095,6 +2154,7 @@ bool launch_small(bool tall, int rb, int av, bool vec, bool t1, dim3 grid, size_
 #undef W4_LAUNCH_16T1
 #undef W4_LAUNCH_T1
 #undef W4_LAUNCH
+#undef W4_ARGS
 }
 
 // The GEMM for every variant (code width, activation type): host validation, plan,
@@ -2157,7 +2217,8 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         q.groups = (int)(K / kGroup);
         q.n_tiles = pl.n_tiles;
         const size_t lds = (size_t)narrow_lds_bytes(q.groups, (int)M, kNarrowWaves);
-        hipLaunchKernelGGL(w4a16_narrow_kernel<kNarrowWaves>, grid, dim3(kNarrowWaves * kWave), lds, s, q);
+        hipLaunchKernelGGL(w4a16_narrow_kernel<kNarrowWaves>, grid, dim3(kNarrowWaves * kWave), lds, s, q.A, q.Wq, q.S,
+                           q.Z, q.C, (int)q.M, (int)q.K, (int)q.N, q.groups);
     } else if (pl.kernel == 3) {
         LargeParams q;
         q.A = (const uint16_t *)A_bf16;
@@ -2176,7 +2237,14 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         q.n_tiles = pl.n_tiles;
         q.m_blocks = pl.m_blocks;
         q.block_rows = pl.tile_m;
-#define W4_LAUNCH_L(RTV) hipLaunchKernelGGL((w4a16_mfma_kernel<RTV>), grid, dim3(kLThreads), 0, s, q)
+        if (q.n_tiles != (N + kLTileN - 1) / kLTileN) {  // the kernel derives the tile count from N
+            set_error("%s: internal error: plan tiles (%d) do not follow from N", name, q.n_tiles);
+            return W4_ERR_PLAN;
+        }
+        const LargeTail tail = {q.C, q.part, q.stride};
+#define W4_LAUNCH_L(RTV)                                                                                          \
+    hipLaunchKernelGGL((w4a16_mfma_kernel<RTV>), grid, dim3(kLThreads), 0, s, q.A, q.Wq, q.S, q.Z, (int)q.M, (int)q.K, \
+                       (int)q.N, q.gps, q.splits, q.block_rows, tail)
         switch ((pl.tile_m + 31) / 32) {
         case 1: W4_LAUNCH_L(1); break;
         case 2: W4_LAUNCH_L(2); break;
@@ -2213,6 +2281,12 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         p.n_tiles = pl.n_tiles;
         p.m_blocks = pl.m_blocks;
         p.full_tiles = pl.full_tiles;
+        // the kernel derives its tile and row-block counts from N, M and its rows per block
+        if (pl.n_tiles != (N + kTileN - 1) / kTileN || pl.m_blocks != (M + pl.tile_m - 1) / pl.tile_m) {
+            set_error("%s: internal error: plan tiles (%d x %d) do not follow from the shape", name, pl.m_blocks,
+                      pl.n_tiles);
+            return W4_ERR_PLAN;
+        }
         // the kernel derives its split-part count from these fields instead of the grid size
         if (pl.workgroups != (int64_t)pl.full_tiles + ((int64_t)pl.m_blocks * pl.n_tiles - pl.full_tiles) * pl.splits) {
             set_error("%s: internal error: plan grid (%lld workgroups) does not match its tiles", name,
