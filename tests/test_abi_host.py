@@ -171,7 +171,10 @@ def test_quantize_validation():
 
 def test_plan_covers_shapes():
     # every shape of the synthetic workloads has a valid plan that tiles N and K exactly;
-    # a balanced wide plan runs whole rounds of 256 tiles unsplit and splits the rest
+    # a balanced wide plan runs whole rounds of 256 tiles unsplit and splits the rest.  The
+    # kernels rely on these identities: they derive their tile and row-block counts from N
+    # and M, and their count of split-part workgroups from the tile, row-block and split
+    # counts, instead of receiving them
     import synth
     seen = set()
     shapes = [(g.M, g.K, g.N, g.bits, g.act4) for wl in synth.WORKLOADS.values() for g in wl.gemms]
