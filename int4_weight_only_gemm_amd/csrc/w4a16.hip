@@ -1517,15 +1517,23 @@ __global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t *__rest
                                                           uint16_t *__restrict__ S, uint8_t *__restrict__ Z,
                                                           int64_t N)
 {
-    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
-    if (c0 >= N) return;
+    // A workgroup takes 256 columns of one group: lane l of wave w holds the column pair
+    // c0, c0 + 1 (c0 = 2 (128 blockIdx.x + 32 w + l % 32)) over the group's rows
+    // 64 (l / 32) .. + 63.  Each half finds its range, the halves swap theirs across the wave,
+    // and both then derive the same parameters; each codes its own 64 rows.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int half = lane >> 5;
+    const int64_t c0 = ((int64_t)blockIdx.x * 128 + wave * 32 + (lane & 31)) * 2;
+    const bool active = c0 < N;  // both halves of a pair share c0, so they agree
     const bool two = c0 + 1 < N;
     const int64_t g = blockIdx.y;
-    const uint16_t *src = W + g * kGroup * N + c0;
-    uint32_t v[kGroup];  // row k: column c0 in the low half, c0 + 1 in the high half
+    const uint16_t *src = W + (g * kGroup + 64 * half) * N + c0;
+    uint32_t v[64];  // row k of the half: column c0 in the low half, c0 + 1 in the high half
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
-        if (VEC) {
+    for (int k = 0; k < 64; ++k) {
+        if (!active) {
+            v[k] = 0;
+        } else if (VEC) {
             v[k] = *(const uint32_t *)(src + k * N);
         } else {
             const uint32_t a = src[k * N], b = src[k * N + (two ? 1 : 0)];  // last column: read twice
@@ -1534,24 +1542,30 @@ __global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t *__rest
     }
     float lo0 = 0.0f, hi0 = 0.0f, lo1 = 0.0f, hi1 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) {
+    for (int k = 0; k < 64; ++k) {
         const f16x2 h = as_h2(v[k]);
         lo0 = fminf(lo0, (float)h.x);
         hi0 = fmaxf(hi0, (float)h.x);
         lo1 = fminf(lo1, (float)h.y);
         hi1 = fmaxf(hi1, (float)h.y);
     }
+    // the other half's range (lane l ^ 32); min and max do not depend on the order
+    lo0 = fminf(lo0, __shfl_xor(lo0, 32));
+    hi0 = fmaxf(hi0, __shfl_xor(hi0, 32));
+    lo1 = fminf(lo1, __shfl_xor(lo1, 32));
+    hi1 = fmaxf(hi1, __shfl_xor(hi1, 32));
+    if (!active) return;
     uint16_t sb0, sb1;
     float s0, z0, s1, z1;
     quant_params(lo0, hi0, sb0, s0, z0);
     quant_params(lo1, hi1, sb1, s1, z1);
     const float r0 = 1.0f / s0, r1 = 1.0f / s1;
-    // the codes convert the packed halves again: keeping 256 converted values from the
-    // range pass alive would double the registers (and cost two thirds of the occupancy)
+    // the codes convert the packed halves again: keeping 128 converted values from the
+    // range pass alive would double the registers
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) asm volatile("" : "+v"(v[k]));
+    for (int k = 0; k < 64; ++k) asm volatile("" : "+v"(v[k]));
 #pragma unroll
-    for (int kb = 0; kb < kGroup / 8; ++kb) {
+    for (int kb = 0; kb < 8; ++kb) {
         uint32_t w0 = 0, w1 = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -1559,7 +1573,7 @@ __global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t *__rest
             w0 |= quant_code((float)h.x, s0, r0, z0) << (4 * j);
             w1 |= quant_code((float)h.y, s1, r1, z1) << (4 * j);
         }
-        uint32_t *dst = Wq + (g * (kGroup / 8) + kb) * N + c0;
+        uint32_t *dst = Wq + (g * (kGroup / 8) + 8 * half + kb) * N + c0;
         if (VEC) {
             *(u32x2 *)dst = u32x2{w0, w1};
         } else {
@@ -1567,6 +1581,7 @@ __global__ __launch_bounds__(256) void w4_quantize_kernel(const uint16_t *__rest
             if (two) dst[1] = w1;
         }
     }
+    if (half != 0) return;
     if (VEC) {
         *(uint32_t *)(S + g * N + c0) = (uint32_t)sb0 | ((uint32_t)sb1 << 16);
         *(uint16_t *)(Z + g * N + c0) = (uint16_t)((uint32_t)z0 | ((uint32_t)z1 << 8));
@@ -2451,7 +2466,7 @@ w4_status w4_quantize(const void *W_f16, uint32_t *Wq, void *scales_f16, uint8_t
     w4_status st = check_device(&dev);
     if (st != W4_OK) return st;
     const bool vec = N % 2 == 0 && aligned(W_f16, 4) && aligned(Wq, 8) && aligned(scales_f16, 4) && aligned(zeros_u4, 2);
-    const dim3 grid((unsigned)((N + 511) / 512), (unsigned)(K / kGroup));
+    const dim3 grid((unsigned)((N + 255) / 256), (unsigned)(K / kGroup));
     if (vec)
         hipLaunchKernelGGL(w4_quantize_kernel<true>, grid, dim3(256), 0, (hipStream_t)stream, (const uint16_t *)W_f16,
                            Wq, (uint16_t *)scales_f16, zeros_u4, N);
