@@ -820,13 +820,15 @@ __host__ __device__ constexpr int narrow_lds_bytes(int groups, int M, int waves)
     return stage > red ? stage : red;
 }
 
+template <int BITS>
 struct NarrowW {
-    uint32_t w[4];  // packed rows 4 st + kq of the lane's column, st = 0..3
-    uint32_t s;     // binary16 scale (low half)
-    uint32_t z;     // zero byte
+    uint32_t w[BITS];  // the lane's column in packed rows: 4-bit 4 st + kq (st = 0..3);
+                       // 8-bit 8 (st / 2) + 2 kq + st % 2 (st = 0..7)
+    uint32_t s;        // binary16 scale (low half)
+    uint32_t z;        // zero byte
 };
 
-template <int WAVES>
+template <int WAVES, int BITS>
 __global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(const uint16_t *A, const uint32_t *Wq,
                                                                       const uint16_t *S, const uint8_t *Z, float *C,
                                                                       int M_, int K_, int N_, int groups)
@@ -855,18 +857,21 @@ __global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(const uint1
     const int64_t nc = n0 + c < N ? n0 + c : N - 1;  // clamped column for loads
 
     Resources rs;
-    rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K / 8 * N * 4), kRsrcWord3);
+    rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K * BITS / 32 * N * 4), kRsrcWord3);
     rs.S = __builtin_amdgcn_make_buffer_rsrc((void *)p.S, (short)0, (int)(p.K / kGroup * N * 2), kRsrcWord3);
     rs.Z = __builtin_amdgcn_make_buffer_rsrc((void *)p.Z, (short)0, (int)(p.K / kGroup * N), kRsrcWord3);
     rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(p.M * p.K * 2), kRsrcWord3);
-    const uint32_t woff = (uint32_t)(((int64_t)kq * N + nc) * 4);
+    // packed rows of the lane's first word: kq (4-bit) or 2 kq (8-bit)
+    const uint32_t woff = (uint32_t)(((int64_t)(BITS == 4 ? kq : 2 * kq) * N + nc) * 4);
     const uint32_t rowbytes = (uint32_t)N * 4;
 
     const int n_my = wave < G ? (G - wave + WAVES - 1) / WAVES : 0;
-    auto load_w = [&](int g, NarrowW &r) {
+    auto load_w = [&](int g, NarrowW<BITS> &r) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-            r.w[st] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, woff, ((uint32_t)g * 16 + 4 * st) * rowbytes, kCacheStream);
+        for (int st = 0; st < BITS; ++st) {
+            const int row = BITS == 4 ? g * 16 + 4 * st : g * 32 + 8 * (st >> 1) + (st & 1);
+            r.w[st] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, woff, (uint32_t)row * rowbytes, kCacheStream);
+        }
         r.s = __builtin_amdgcn_raw_buffer_load_b16(rs.S, (uint32_t)(nc * 2), (uint32_t)g * (uint32_t)N * 2, 0);
         r.z = __builtin_amdgcn_raw_buffer_load_b8(rs.Z, (uint32_t)nc, (uint32_t)g * (uint32_t)N, 0);
     };
@@ -889,7 +894,7 @@ __global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(const uint1
         const int q = q0 + drow;
         const int e = row16_max(chunk_max_exp(v));
         const int x = 142 - max(e, 1);
-        const u32x4 h = convert_chunk<4>(v, x);
+        const u32x4 h = convert_chunk<BITS>(v, x);
         if (q < pairs) {
             *(u32x4 *)(lds + q * kARowBytes + kc * 16) = h;
             if (kc == 0) {
@@ -910,20 +915,36 @@ __global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(const uint1
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int zero_off = narrow_zero_offset(G, M);
     const int a_lane = c < M ? c * kARowBytes + kq * 16 : -1;  // -1: a row past M
-    auto compute = [&](int g, const NarrowW &r) {
-        uint32_t magic;
-        asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
-        const uint32_t z = r.z & 0xFu;
-        uint32_t zlo = (0xE400u | z) * 0x00010001u, zhi = (0xD400u | (z << 4)) * 0x00010001u;
-        asm volatile("" : "+v"(zlo), "+v"(zhi));
+    auto compute = [&](int g, const NarrowW<BITS> &r) {
         const int gbase = g * M * kARowBytes;
         f32x4 P;
+        if constexpr (BITS == 4) {
+            uint32_t magic;
+            asm("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+            const uint32_t z = r.z & 0xFu;
+            uint32_t zlo = (0xE400u | z) * 0x00010001u, zhi = (0xD400u | (z << 4)) * 0x00010001u;
+            asm volatile("" : "+v"(zlo), "+v"(zhi));
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int ao = a_lane >= 0 ? gbase + a_lane + st * 64 : zero_off;
-            const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds + ao));
-            const f16x8 b_op = unpack8(r.w[st], zlo, zhi, magic);
-            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P, 0, 0, 0);
+            for (int st = 0; st < 4; ++st) {
+                const int ao = a_lane >= 0 ? gbase + a_lane + st * 64 : zero_off;
+                const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds + ao));
+                const f16x8 b_op = unpack8(r.w[st], zlo, zhi, magic);
+                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, st == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P, 0, 0, 0);
+            }
+        } else {
+            uint32_t magic, sel01, sel23;
+            asm("v_mov_b32 %0, 0x64646464" : "=v"(magic));
+            asm("s_mov_b32 %0, 0x04010400" : "=s"(sel01));  // bytes: q0, 0x64, q1, 0x64
+            asm("s_mov_b32 %0, 0x04030402" : "=s"(sel23));  // bytes: q2, 0x64, q3, 0x64
+            uint32_t zneg = (0xE400u | (r.z & 0xFFu)) * 0x00010001u;  // -(1024 + z)
+            asm volatile("" : "+v"(zneg));
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ao = a_lane >= 0 ? gbase + a_lane + ks * 64 : zero_off;
+                const f16x8 a_op = __builtin_bit_cast(f16x8, *(const u32x4 *)(lds + ao));
+                const f16x8 b_op = unpack8_w8(r.w[2 * ks], r.w[2 * ks + 1], zneg, magic, sel01, sel23);
+                P = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_op, b_op, ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : P, 0, 0, 0);
+            }
         }
         const int4 xr = *(const int4 *)(lds + narrow_exp_offset(G, M) + (g * kTileM + 4 * kq) * 4);
         const float sv = (float)__builtin_bit_cast(_Float16, (uint16_t)r.s);
@@ -938,7 +959,7 @@ __global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(const uint1
     // the groups; any further groups are loaded and computed one at a time.
     auto run = [&](auto kconst) {
         constexpr int KG = decltype(kconst)::value;
-        NarrowW wr[KG > 0 ? KG : 1];
+        NarrowW<BITS> wr[KG > 0 ? KG : 1];
         // the first passes' activation loads come before the weights: loads complete in
         // issue order, so the staging below then overlaps the weight stream
         constexpr int kPre = 5;
@@ -984,7 +1005,7 @@ __global__ __launch_bounds__(WAVES * kWave) void w4a16_narrow_kernel(const uint1
     default: run(std::integral_constant<int, kNarrowMaxGroups>{}); break;
     }
     for (int u = kNarrowMaxGroups; u < n_my; ++u) {
-        NarrowW r;
+        NarrowW<BITS> r;
         load_w(wave + WAVES * u, r);
         compute(wave + WAVES * u, r);
     }
@@ -2084,6 +2105,17 @@ void make_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
         make_small_plan(M, K, N, pl);
 }
 
+// 8-bit codes: narrow outputs on the narrow-tile kernel as for 4-bit codes (the same rule:
+// the tile count, the groups per wave and the staged activations do not depend on the code
+// width), everything else on the small-M kernel.
+void make_plan8(int64_t M, int64_t K, int64_t N, w4_plan *pl)
+{
+    if (narrow_eligible(M, K, N))
+        make_narrow_plan(M, K, N, pl);
+    else
+        make_small_plan(M, K, N, pl, 8);
+}
+
 size_t plan_lds_bytes(int64_t M, const w4_plan &pl)
 {
     const int rows = M < pl.tile_m ? (int)M : pl.tile_m;
@@ -2109,7 +2141,7 @@ bool small_instance_exists(int rb, int av, int bits, bool a4)
 bool plan_has_instance(int64_t M, const w4_plan &pl, int bits, bool a4)
 {
     if (pl.kernel == 3) return !a4 && bits == 4 && pl.tile_m >= 1 && pl.tile_m <= kLMaxRT * 32;
-    if (pl.kernel == 8) return !a4 && bits == 4 && M <= kTileM && pl.tile_n == kNarrowN;
+    if (pl.kernel == 8) return !a4 && (bits == 4 || bits == 8) && M <= kTileM && pl.tile_n == kNarrowN;
     if (pl.tile_m % kTileM != 0) return false;
     const int rows = M < pl.tile_m ? (int)M : pl.tile_m;
     return small_instance_exists(pl.tile_m / kTileM, (rows + 3) / 4, bits, a4);
@@ -2198,8 +2230,10 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
     if (st != W4_OK) return st;
 
     w4_plan pl;
-    if (bits == 8 || a4)
+    if (a4)
         make_small_plan(M, K, N, &pl, bits, a4);
+    else if (bits == 8)
+        make_plan8(M, K, N, &pl);
     else
         make_plan(M, K, N, &pl);
     st = check_plan(name, M, pl, bits, a4);
@@ -2232,8 +2266,12 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         q.groups = (int)(K / kGroup);
         q.n_tiles = pl.n_tiles;
         const size_t lds = (size_t)narrow_lds_bytes(q.groups, (int)M, kNarrowWaves);
-        hipLaunchKernelGGL(w4a16_narrow_kernel<kNarrowWaves>, grid, dim3(kNarrowWaves * kWave), lds, s, q.A, q.Wq, q.S,
-                           q.Z, q.C, (int)q.M, (int)q.K, (int)q.N, q.groups);
+        if (bits == 8)
+            hipLaunchKernelGGL((w4a16_narrow_kernel<kNarrowWaves, 8>), grid, dim3(kNarrowWaves * kWave), lds, s, q.A,
+                               q.Wq, q.S, q.Z, q.C, (int)q.M, (int)q.K, (int)q.N, q.groups);
+        else
+            hipLaunchKernelGGL((w4a16_narrow_kernel<kNarrowWaves, 4>), grid, dim3(kNarrowWaves * kWave), lds, s, q.A,
+                               q.Wq, q.S, q.Z, q.C, (int)q.M, (int)q.K, (int)q.N, q.groups);
     } else if (pl.kernel == 3) {
         LargeParams q;
         q.A = (const uint16_t *)A_bf16;
@@ -2442,7 +2480,7 @@ w4_status w8a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out)
     }
     w4_status st = validate_gemm_shape(M, K, N, 8);
     if (st != W4_OK) return st;
-    make_small_plan(M, K, N, out, 8);
+    make_plan8(M, K, N, out);
     return check_plan("w8a16_plan", M, *out, 8, false);
 }
 

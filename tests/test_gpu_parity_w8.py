@@ -72,6 +72,40 @@ def test_split_k_shapes8(orc, M, K, N):
     check(C[:, cols], Cr, Cabs, f"w8 split M={M} K={K} N={N}")
 
 
+# ------------------------------------------------------------- narrow-tile kernel
+NARROW8_SHAPES = [(1, 8192, 4095), (5, 3584, 3584), (8, 3584, 1000), (16, 1792, 300), (3, 128, 17),
+                  (7, 640, 4096), (2, 8064, 33), (4, 1024, 1), (1, 1536, 2048)]
+
+
+@pytest.mark.parametrize("M,K,N", NARROW8_SHAPES)
+def test_narrow_kernel_every_element8(orc, M, K, N):
+    # 8-bit codes on the narrow-tile kernel: 64 groups (eight per wave, the most a wave
+    # holds), one group, ragged N down to a single column, 16 rows, 256 tiles; NaN-poisoned
+    # C, every element against the oracle
+    p = w4.plan(M, K, N, bits=8)
+    log(f"w8 narrow M={M} K={K} N={N} plan={p}")
+    assert p["kernel"] == 8 and p["tile_n"] == 16 and p["splits"] == 1
+    x = gen8(M, K, N, seed=63)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    C = run8(to_dev(x), out=out).cpu().numpy()
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, bits=8)
+    check(C, Cr, Cabs, f"w8 narrow M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(5, 9216, 65), (13, 8320, 7), (9, 128, 4160), (1, 16384, 3), (16, 8448, 130)])
+def test_small_kernel_ragged8(orc, M, K, N):
+    # rows in one 16-row block on the 8-bit small-M kernel (more than 64 groups, or more than
+    # 256 narrow tiles): ragged N, every element
+    p = w4.plan(M, K, N, bits=8)
+    log(f"w8 small-M M={M} K={K} N={N} plan={p}")
+    assert p["kernel"] in (4, 5)
+    x = gen8(M, K, N, seed=64)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    C = run8(to_dev(x), out=out).cpu().numpy()
+    Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, bits=8)
+    check(C, Cr, Cabs, f"w8 small-M M={M} K={K} N={N}")
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 1536, 17920), (5, 1024, 19200), (3, 2048, 19198)])
 def test_balanced_wide_plan8(orc, M, K, N):
     p = w4.plan(M, K, N, bits=8)
