@@ -1859,7 +1859,8 @@ struct Choice {
     double us;
 };
 
-Choice score(const Variant &v, int64_t base, int groups, int splits, int av, int64_t K, int64_t N, int bits)
+Choice score(const Variant &v, int64_t base, int groups, int splits, int av, int64_t K, int64_t N, int bits,
+             bool simd_sum = false)
 {
     Choice c = {&v, splits, 1e30};
     const int gps = (groups + splits - 1) / splits;
@@ -1869,7 +1870,15 @@ Choice score(const Variant &v, int64_t base, int groups, int splits, int av, int
     const double waves_per_simd = (double)v.waves * wg_per_cu / 4;
     const double t_group = kUsPerGroup * waves_per_simd * (1.0 + kRowsFactor * (av - 1));
     const int per_wave = (gps + v.waves - 1) / v.waves;
-    const double compute = per_wave * t_group;
+    double compute = per_wave * t_group;
+    if (simd_sum) {
+        // the busiest SIMD runs waves s, s + 4, ... of each workgroup and wave w holds
+        // ceil((gps - w) / waves) groups: uneven counts cost that SIMD their sum, not
+        // per_wave on each of its waves (which over-charges the 12-wave shape)
+        int simd_groups = 0;
+        for (int w = 0; w < v.waves; w += 4) simd_groups += gps > w ? (gps - w + v.waves - 1) / v.waves : 0;
+        compute = simd_groups * (t_group / (v.waves / 4));
+    }
     const int active_waves_per_wg = gps < v.waves ? gps : v.waves;
     const double inflight = (double)wgs * active_waves_per_wg * (per_wave < 2 ? per_wave : 2) * group_bytes(bits);
     double rate = inflight / (kUsLatency * 1e-6) / 1e9;  // GB/s
@@ -2008,11 +2017,18 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     // measured faster at every split count (8960x1536 at M=1: 8.60 against 9.41 us at 4
     // splits, 7.39 against 7.76 at 6; qkv-sized 1536x2048: 5.24 against 5.59 us).
     const bool wide_first = bits == 8 && av == 1;
+    // Several 16-row blocks of bfloat16 activations (M = 17..63): the per-SIMD group sum.
+    // With it the 12-wave shape takes qkv- and o-sized outputs at the same split count, as
+    // measured 4-15% faster (M = 24: 3584x4608 10.45 -> 9.35 us, 3584x3584 9.27 -> 8.75,
+    // 8960x1536 9.29 -> 8.88; M = 40: 3584x4608 10.48 -> 9.38, 3584x3584 10.37 -> 9.20,
+    // 4096x4096 11.67 -> 9.95; M = 56: 3584x3584 10.48 -> 9.31).  At one block the plans
+    // keep the original estimate, which their forced-plan sweeps confirmed.
+    const bool simd_sum = m_blocks > 1 && bits == 4 && !a4;
     for (const Variant *v : {wide_first ? &wide : &tall, wide_first ? &tall : &wide}) {
         for (int sp = 1; sp <= groups; ++sp) {
             const int gps = (groups + sp - 1) / sp;
             if ((groups + gps - 1) / gps != sp) continue;
-            const Choice c = score(*v, base, groups, sp, av, K, N, bits);
+            const Choice c = score(*v, base, groups, sp, av, K, N, bits, simd_sum);
             if (c.us < best.us * 0.98) best = c;
         }
     }
@@ -2025,7 +2041,7 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     // 1-3% faster on 16-row blocks at M = 24..60, 12-14% on 32-row blocks).
     const int best_gps = (groups + best.splits - 1) / best.splits;
     if (best.v == &tall && (best_gps < tall.waves || (best_gps == tall.waves && m_blocks == 1 && rows == kTileM))) {
-        const Choice w = score(wide, base, groups, best.splits, av, K, N, bits);
+        const Choice w = score(wide, base, groups, best.splits, av, K, N, bits, simd_sum);
         if (w.us <= best.us * 1.02) best = w;
     }
     // Balanced wide plan.  When the plain wide plan wins and its tiles fill r whole rounds of
