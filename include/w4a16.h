@@ -232,13 +232,24 @@ typedef struct w4_plan {
     int m_blocks;           /* row blocks of tile_m                                          */
     int n_tiles;            /* column tiles of tile_n                                        */
     int splits;             /* K splits across workgroups (1 = no workspace)                */
-    int groups_per_split;   /* 128-wide K groups handled by one workgroup of a split tile    */
+    int groups_per_split;   /* 128-wide K groups handled by one workgroup of a split tile
+                               (kernel 3: (tile, group) steps per workgroup)                 */
     int full_tiles;         /* kernels 1, 4, 6: tiles 0..full_tiles-1 (tile t is row block
                                t % m_blocks of column tile t / m_blocks) run
                                unsplit, one workgroup each, and only the other tiles are
                                split (a multiple of 256: whole rounds of CUs); 0 otherwise  */
-    int64_t workgroups;     /* grid size: full_tiles + (m_blocks*n_tiles - full_tiles)*splits */
+    int64_t workgroups;     /* grid size: full_tiles + (m_blocks*n_tiles - full_tiles)*splits,
+                               except kernel 3: ceil(m_blocks*n_tiles*group_stride /
+                               groups_per_split)                                              */
     int64_t workspace_bytes;/* split-K workspace needed (0 when splits == 1)                 */
+    int64_t group_stride;   /* kernel 3 (0 for the others): the (tile, group) steps are
+                               numbered tile-major with this many numbers per tile (the
+                               K/128 groups, then unused numbers), and workgroup w takes
+                               steps w*groups_per_split .. +groups_per_split-1.  Equal to
+                               splits*groups_per_split, each workgroup works in one tile (a
+                               K split); equal to the group count, the steps are shared out
+                               evenly and a workgroup may finish one tile and start the
+                               next.  splits is then the most workgroups any tile has     */
 } w4_plan;
 
 w4_status w4a16_plan(int64_t M, int64_t K, int64_t N, w4_plan *out);

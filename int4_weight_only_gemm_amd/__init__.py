@@ -66,6 +66,7 @@ class Plan(ctypes.Structure):
         ("full_tiles", ctypes.c_int),
         ("workgroups", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
+        ("group_stride", ctypes.c_int64),
     ]
 
     def as_dict(self) -> Dict[str, int]:

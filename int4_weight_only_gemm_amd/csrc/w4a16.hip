@@ -1053,6 +1053,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kLWaves = 8;
 constexpr int kLTileN = kLWaves * 32;  // 256 columns per workgroup
 constexpr int kLMaxRT = 5;             // 32 to 160 rows per workgroup (row tiles of 32)
+constexpr int kLargeSharedMaxRT = 2;   // most row tiles of a workgroup that may hold two tiles' steps
 constexpr int kLThreads = kLWaves * kWave;
 
 struct LargeParams {
@@ -1174,7 +1175,7 @@ struct LargeW {
 template <int RT>
 __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S, const uint8_t *Z, int M_, int K_,
-                       int N_, int groups_per_split, int splits, int block_rows, LargeTail tail)
+                       int N_, int groups_per_split, int group_stride, int block_rows, LargeTail tail)
 {
     constexpr int kRows = RT * 32;
     constexpr int kBuf = kRows * kARowBytes;
@@ -1194,208 +1195,241 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
     p.K = K_;
     p.N = N_;
     p.groups = K_ / kGroup;
-    p.splits = splits;
+    p.splits = 0;  // not used by the kernel
     p.gps = groups_per_split;
     p.n_tiles = (N_ + kLTileN - 1) / kLTileN;
-    p.m_blocks = 0;  // not used by the kernel
+    p.m_blocks = RT <= kLargeSharedMaxRT ? (M_ + block_rows - 1) / block_rows : 0;  // (not needed otherwise)
     p.block_rows = block_rows;
 
-    const uint32_t logical = blockIdx.x;
-    const int sp = (int)(logical % (uint32_t)p.splits);
-    const uint32_t tile = logical / (uint32_t)p.splits;
-    const int nt = (int)(tile % (uint32_t)p.n_tiles);
-    const int mb = (int)(tile / (uint32_t)p.n_tiles);
-    const int64_t m0 = (int64_t)mb * p.block_rows;
-    const int64_t m_end = m0 + p.block_rows < p.M ? m0 + p.block_rows : p.M;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int c = lane & 31, h = lane >> 5;
     const int64_t N = p.N;
-    const int64_t col = (int64_t)nt * kLTileN + wave * 32 + c;
-    const int64_t colc = col < N ? col : N - 1;
-
-    const int g_begin = sp * p.gps;
-    const int g_end = min(p.groups, g_begin + p.gps);
 
     Resources rs;
     rs.W = __builtin_amdgcn_make_buffer_rsrc((void *)p.Wq, (short)0, (int)(p.K / 8 * N * 4), kRsrcWord3);
     rs.S = __builtin_amdgcn_make_buffer_rsrc((void *)p.S, (short)0, (int)(p.K / kGroup * N * 2), kRsrcWord3);
     rs.Z = __builtin_amdgcn_make_buffer_rsrc((void *)p.Z, (short)0, (int)(p.K / kGroup * N), kRsrcWord3);
     rs.A = __builtin_amdgcn_make_buffer_rsrc((void *)p.A, (short)0, (int)(p.M * p.K * 2), kRsrcWord3);
-    const uint32_t woff = (uint32_t)((h * N + colc) * 4);
-    const uint32_t soff = (uint32_t)(colc * 2), zoff = (uint32_t)colc;
     const uint32_t rowbytes = (uint32_t)N * 4;
 
-    // Activation staging: chunk id = thread + 512 j is (row id / 16, 16-byte chunk id % 16)
-    // of the group; rows outside the block read row m_end - 1 (never stored).
-    uint32_t aoff[kAChunks];
-    int alds[kAChunks];
-#pragma unroll
-    for (int j = 0; j < kAChunks; ++j) {
-        const int id = threadIdx.x + kLThreads * j;
-        const int row = id >> 4, kc = id & 15;
-        const int64_t srow = m0 + row < m_end ? m0 + row : m_end - 1;
-        aoff[j] = (uint32_t)((srow * p.K + kc * 8) * 2);
-        alds[j] = row * kARowBytes + kc * 16;
-    }
-    auto load_a = [&](int g, u32x4 (&ar)[kAChunks]) {
-#pragma unroll
-        for (int j = 0; j < kAChunks; ++j) ar[j] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[j], (uint32_t)g * (kGroup * 2), 0);
-    };
-    auto store_a = [&](int buf, const u32x4 (&ar)[kAChunks]) {
-#pragma unroll
-        for (int j = 0; j < kAChunks; ++j) *(u32x4 *)(lds + buf * kBuf + alds[j]) = ar[j];
-    };
-    auto load_w = [&](int g, LargeW &r) {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            r.w[ks] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, woff, ((uint32_t)g * 16 + 2 * ks) * rowbytes, kCacheStream);
-        r.s = __builtin_amdgcn_raw_buffer_load_b16(rs.S, soff, (uint32_t)g * (uint32_t)N * 2, 0);
-        r.z = __builtin_amdgcn_raw_buffer_load_b8(rs.Z, zoff, (uint32_t)g * (uint32_t)N, 0);
-    };
-    auto scale_of = [](const LargeW &r) { return (float)__builtin_bit_cast(_Float16, (uint16_t)r.s); };
+    // Work assignment.  The (tile, group) steps are numbered tile-major, tile t (row block
+    // t / n_tiles, column tile t % n_tiles) owning steps t * group_stride .. + groups - 1
+    // (group_stride >= groups; numbers past a tile's groups are skipped).  Workgroup w takes
+    // steps w * groups_per_split .. + groups_per_split - 1: with group_stride = splits *
+    // groups_per_split that is one tile's split, with group_stride = groups the workgroups
+    // share out all the steps evenly and one may finish a tile and go on to the next.  Each
+    // piece of a tile (a segment) is accumulated on its own; a segment covering the whole
+    // tile goes to C, any other to the partial-product slice numbered by the workgroup's
+    // place among the tile's workgroups (w - floor(t * group_stride / groups_per_split)).
+    // Wider row blocks only ever take whole-tile splits (group_stride = splits * gps, checked
+    // on the host): a workgroup's steps lie in one tile, so neither the step count nor the
+    // end of the range is needed (one division less on the way to the first loads).
+    constexpr bool kShared = RT <= kLargeSharedMaxRT;
+    const uint32_t total = kShared ? (uint32_t)p.m_blocks * (uint32_t)p.n_tiles * (uint32_t)group_stride : 0u;
+    uint32_t u = blockIdx.x * (uint32_t)p.gps;
+    const uint32_t u_end = u + (uint32_t)p.gps < total ? u + (uint32_t)p.gps : total;
+    for (;;) {
+        // (uniform values: the divisions run on the vector unit, so their results are moved
+        // back to scalar registers)
+        const uint32_t tile = __builtin_amdgcn_readfirstlane(u / (uint32_t)group_stride);
+        const int g_begin = (int)(u - tile * (uint32_t)group_stride);
+        int g_stop = g_begin + p.gps;
+        if constexpr (kShared)
+            g_stop = g_begin + (int)(u_end - u) < group_stride ? g_begin + (int)(u_end - u) : group_stride;
+        const int g_end = min(p.groups, g_stop);
+        const int slot = __builtin_amdgcn_readfirstlane(blockIdx.x - tile * (uint32_t)group_stride / (uint32_t)p.gps);
+        const int nt = __builtin_amdgcn_readfirstlane(tile % (uint32_t)p.n_tiles);
+        const int mb = __builtin_amdgcn_readfirstlane(tile / (uint32_t)p.n_tiles);
+        // Lane constants are derived anew in each segment: hoisted out of this loop they
+        // would stay live through the group loop and cost it registers.
+        uint32_t tid = threadIdx.x;
+        if constexpr (kShared) asm volatile("" : "+v"(tid));
+        const int lane = (int)(tid & 63);
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int c = lane & 31, h = lane >> 5;
+        const int64_t m0 = (int64_t)mb * p.block_rows;
+        const int64_t m_end = m0 + p.block_rows < p.M ? m0 + p.block_rows : p.M;
+        const int64_t col = (int64_t)nt * kLTileN + wave * 32 + c;
+        const int64_t colc = col < N ? col : N - 1;
+        const uint32_t woff = (uint32_t)((h * N + colc) * 4);
+        const uint32_t soff = (uint32_t)(colc * 2), zoff = (uint32_t)colc;
 
-    f32x16 acc[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[rt][v] = 0.f;
-
-    // A operand of (row tile rt, k-step ks): row rt*32 + c, k = 16 ks + 8 h .. + 7
-    const int a_lane = c * kARowBytes + h * 16;
-
-    // Two register sets for packed weights (X, Y) and two for dequantized operands (B0, B1)
-    // alternate between consecutive groups (the loop is unrolled by two), so no register
-    // set is ever copied: a copy would make the compiler wait for in-flight loads early.
-    u32x4 ar[kAChunks];
-    LargeW wx, wy;
-    bf16x8 B0[8], B1[8];
-    float sc0, sc1;
-
-    // One group: MFMAs on Bc (group g), dequantize Wn (group g + 1) into Bn, load group
-    // g + 2's weights into Wl and group g + 1's activations into ar.
-    auto group_step = [&](int g, LargeW &Wn, LargeW &Wl, const bf16x8 (&Bc)[8], bf16x8 (&Bn)[8],
-                          float sc, float &scn) {
-        const int buf = (g - g_begin) & 1;
-        const int gn1 = g + 1 < g_end ? g + 1 : g;  // clamped: the tail reloads, no branch
-        const int gn2 = g + 2 < g_end ? g + 2 : gn1;
-        load_a(gn1, ar);
-        load_w(gn2, Wl);
-        __builtin_amdgcn_sched_barrier(0);
-        // Pin this group's dequantization inside this group: without it the compiler may
-        // hoist it into the previous group, where it would wait for loads just issued.
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Wn.w[ks]));
-        asm volatile("" : "+v"(Wn.z), "+v"(Wn.s));
-
-        const char *abase = lds + buf * kBuf + a_lane;
-        const uint32_t zzn = (Wn.z & 0xFu) * 0x01010101u;
-        constexpr int kAhead = 2;  // A operands read two MFMA steps ahead
-        bf16x8 ring[kAhead + 1];
-        auto a_at = [&](int n) {
-            return *(const bf16x8 *)(abase + large_step_rt<RT>(n) * 32 * kARowBytes + large_step_ks<RT>(n) * 32);
+        // Activation staging: chunk id = thread + 512 j is (row id / 16, 16-byte chunk id % 16)
+        // of the group; rows outside the block read row m_end - 1 (never stored).
+        uint32_t aoff[kAChunks];
+        int alds[kAChunks];
+    #pragma unroll
+        for (int j = 0; j < kAChunks; ++j) {
+            const int id = (int)tid + kLThreads * j;
+            const int row = id >> 4, kc = id & 15;
+            const int64_t srow = m0 + row < m_end ? m0 + row : m_end - 1;
+            aoff[j] = (uint32_t)((srow * p.K + kc * 8) * 2);
+            alds[j] = row * kARowBytes + kc * 16;
+        }
+        auto load_a = [&](int g, u32x4 (&ar)[kAChunks]) {
+    #pragma unroll
+            for (int j = 0; j < kAChunks; ++j) ar[j] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[j], (uint32_t)g * (kGroup * 2), 0);
         };
-#pragma unroll
-        for (int i = 0; i < kAhead; ++i) ring[i] = a_at(i);
-        // MFMA step n runs (row tile, k-step) = (large_step_rt, large_step_ks): the row tiles
-        // go in segments of one or two, and a segment of two interleaves its tiles' chains
-        // per k-step (two independent accumulation chains hide each other's MFMA latency).
-        // After each MFMA an even share of the VALU work: word n / RT's dequantization in
-        // pieces over RT steps, and, from the segment's second step on, the rescale of the
-        // previous segment's row tiles.  A scheduling barrier after each step keeps this
-        // order.  Row tile rt accumulates in chain rt % 2 and is rescaled from Q[rt % 2].
-        Unpack8 u;
-        f32x16 P[2], Q[2];
-#pragma unroll
-        for (int sg = 0; sg < large_segments<RT>(); ++sg) {
-            const int r0 = large_seg_first<RT>(sg), cnt = large_seg_count<RT>(sg);
-            const int base = 8 * r0, len = 8 * cnt;
-            const int pr0 = sg > 0 ? large_seg_first<RT>(sg - 1) : 0;
-            const int pending = sg > 0 ? 16 * large_seg_count<RT>(sg - 1) : 0;
-#pragma unroll
-            for (int i = 0; i < len; ++i) {
-                const int n = base + i;
-                const int rt = large_step_rt<RT>(n), ks = large_step_ks<RT>(n);
-                if (n + kAhead < kSteps) ring[(n + kAhead) % (kAhead + 1)] = a_at(n + kAhead);
-                const bf16x8 a = ring[n % (kAhead + 1)];
-                f32x16 &Pc = P[rt & 1];
-                if (ks == 0) {
-                    const f32x16 zero = {};
-                    Pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], zero, 0, 0, 0);
-                } else {
-                    Pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], Pc, 0, 0, 0);
-                }
-                const int word = n / RT, l = n % RT;
-#pragma unroll
-                for (int pc = l * 5 / RT; pc < (l + 1) * 5 / RT; ++pc) unpack8_piece(pc, u, Wn.w[word], zzn);
-                if (l == RT - 1) Bn[word] = __builtin_bit_cast(bf16x8, u.r);
-                // the previous segment's partials, spread over steps 1 .. len - 1
-                if (pending > 0 && i > 0) {
-                    const int f0 = (i - 1) * pending / (len - 1), f1 = i * pending / (len - 1);
-#pragma unroll
-                    for (int f = f0; f < f1; ++f) {
-                        const int tr = pr0 + f / 16, v = f % 16;
-                        acc[tr][v] = __builtin_fmaf(sc, Q[tr & 1][v], acc[tr][v]);
+        auto store_a = [&](int buf, const u32x4 (&ar)[kAChunks]) {
+    #pragma unroll
+            for (int j = 0; j < kAChunks; ++j) *(u32x4 *)(lds + buf * kBuf + alds[j]) = ar[j];
+        };
+        auto load_w = [&](int g, LargeW &r) {
+    #pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                r.w[ks] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, woff, ((uint32_t)g * 16 + 2 * ks) * rowbytes, kCacheStream);
+            r.s = __builtin_amdgcn_raw_buffer_load_b16(rs.S, soff, (uint32_t)g * (uint32_t)N * 2, 0);
+            r.z = __builtin_amdgcn_raw_buffer_load_b8(rs.Z, zoff, (uint32_t)g * (uint32_t)N, 0);
+        };
+        auto scale_of = [](const LargeW &r) { return (float)__builtin_bit_cast(_Float16, (uint16_t)r.s); };
+
+        f32x16 acc[RT];
+    #pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+    #pragma unroll
+            for (int v = 0; v < 16; ++v) acc[rt][v] = 0.f;
+
+        // A operand of (row tile rt, k-step ks): row rt*32 + c, k = 16 ks + 8 h .. + 7
+        const int a_lane = c * kARowBytes + h * 16;
+
+        // Two register sets for packed weights (X, Y) and two for dequantized operands (B0, B1)
+        // alternate between consecutive groups (the loop is unrolled by two), so no register
+        // set is ever copied: a copy would make the compiler wait for in-flight loads early.
+        u32x4 ar[kAChunks];
+        LargeW wx, wy;
+        bf16x8 B0[8], B1[8];
+        float sc0, sc1;
+
+        // One group: MFMAs on Bc (group g), dequantize Wn (group g + 1) into Bn, load group
+        // g + 2's weights into Wl and group g + 1's activations into ar.
+        auto group_step = [&](int g, LargeW &Wn, LargeW &Wl, const bf16x8 (&Bc)[8], bf16x8 (&Bn)[8],
+                              float sc, float &scn) {
+            const int buf = (g - g_begin) & 1;
+            const int gn1 = g + 1 < g_end ? g + 1 : g;  // clamped: the tail reloads, no branch
+            const int gn2 = g + 2 < g_end ? g + 2 : gn1;
+            load_a(gn1, ar);
+            load_w(gn2, Wl);
+            __builtin_amdgcn_sched_barrier(0);
+            // Pin this group's dequantization inside this group: without it the compiler may
+            // hoist it into the previous group, where it would wait for loads just issued.
+    #pragma unroll
+            for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Wn.w[ks]));
+            asm volatile("" : "+v"(Wn.z), "+v"(Wn.s));
+
+            const char *abase = lds + buf * kBuf + a_lane;
+            const uint32_t zzn = (Wn.z & 0xFu) * 0x01010101u;
+            constexpr int kAhead = 2;  // A operands read two MFMA steps ahead
+            bf16x8 ring[kAhead + 1];
+            auto a_at = [&](int n) {
+                return *(const bf16x8 *)(abase + large_step_rt<RT>(n) * 32 * kARowBytes + large_step_ks<RT>(n) * 32);
+            };
+    #pragma unroll
+            for (int i = 0; i < kAhead; ++i) ring[i] = a_at(i);
+            // MFMA step n runs (row tile, k-step) = (large_step_rt, large_step_ks): the row tiles
+            // go in segments of one or two, and a segment of two interleaves its tiles' chains
+            // per k-step (two independent accumulation chains hide each other's MFMA latency).
+            // After each MFMA an even share of the VALU work: word n / RT's dequantization in
+            // pieces over RT steps, and, from the segment's second step on, the rescale of the
+            // previous segment's row tiles.  A scheduling barrier after each step keeps this
+            // order.  Row tile rt accumulates in chain rt % 2 and is rescaled from Q[rt % 2].
+            Unpack8 u;
+            f32x16 P[2], Q[2];
+    #pragma unroll
+            for (int sg = 0; sg < large_segments<RT>(); ++sg) {
+                const int r0 = large_seg_first<RT>(sg), cnt = large_seg_count<RT>(sg);
+                const int base = 8 * r0, len = 8 * cnt;
+                const int pr0 = sg > 0 ? large_seg_first<RT>(sg - 1) : 0;
+                const int pending = sg > 0 ? 16 * large_seg_count<RT>(sg - 1) : 0;
+    #pragma unroll
+                for (int i = 0; i < len; ++i) {
+                    const int n = base + i;
+                    const int rt = large_step_rt<RT>(n), ks = large_step_ks<RT>(n);
+                    if (n + kAhead < kSteps) ring[(n + kAhead) % (kAhead + 1)] = a_at(n + kAhead);
+                    const bf16x8 a = ring[n % (kAhead + 1)];
+                    f32x16 &Pc = P[rt & 1];
+                    if (ks == 0) {
+                        const f32x16 zero = {};
+                        Pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], zero, 0, 0, 0);
+                    } else {
+                        Pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], Pc, 0, 0, 0);
                     }
+                    const int word = n / RT, l = n % RT;
+    #pragma unroll
+                    for (int pc = l * 5 / RT; pc < (l + 1) * 5 / RT; ++pc) unpack8_piece(pc, u, Wn.w[word], zzn);
+                    if (l == RT - 1) Bn[word] = __builtin_bit_cast(bf16x8, u.r);
+                    // the previous segment's partials, spread over steps 1 .. len - 1
+                    if (pending > 0 && i > 0) {
+                        const int f0 = (i - 1) * pending / (len - 1), f1 = i * pending / (len - 1);
+    #pragma unroll
+                        for (int f = f0; f < f1; ++f) {
+                            const int tr = pr0 + f / 16, v = f % 16;
+                            acc[tr][v] = __builtin_fmaf(sc, Q[tr & 1][v], acc[tr][v]);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                for (int c = 0; c < cnt; ++c) {
+                    Q[(r0 + c) & 1] = P[(r0 + c) & 1];
+                    // stage one chunk of the next group's activations per row tile, so the LDS
+                    // writes spread over the group instead of queueing behind its reads at the end
+                    *(u32x4 *)(lds + (buf ^ 1) * kBuf + alds[r0 + c]) = ar[r0 + c];
+                }
             }
-#pragma unroll
-            for (int c = 0; c < cnt; ++c) {
-                Q[(r0 + c) & 1] = P[(r0 + c) & 1];
-                // stage one chunk of the next group's activations per row tile, so the LDS
-                // writes spread over the group instead of queueing behind its reads at the end
-                *(u32x4 *)(lds + (buf ^ 1) * kBuf + alds[r0 + c]) = ar[r0 + c];
+            scn = scale_of(Wn);
+            // ... and keep it from sinking into the next group: the operands are complete here.
+    #pragma unroll
+            for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Bn[ks]));
+            // The barrier comes as soon as this wave's LDS traffic for the group is done; the
+            // last row tile's rescale (which waits for its MFMAs) follows it.
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            {
+                constexpr int last = large_segments<RT>() - 1;
+                const int r0 = large_seg_first<RT>(last), cnt = large_seg_count<RT>(last);
+    #pragma unroll
+                for (int c = 0; c < cnt; ++c)
+    #pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        acc[r0 + c][v] = __builtin_fmaf(sc, Q[(r0 + c) & 1][v], acc[r0 + c][v]);
             }
-        }
-        scn = scale_of(Wn);
-        // ... and keep it from sinking into the next group: the operands are complete here.
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Bn[ks]));
-        // The barrier comes as soon as this wave's LDS traffic for the group is done; the
-        // last row tile's rescale (which waits for its MFMAs) follows it.
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        load_a(g_begin, ar);
+        load_w(g_begin, wy);
+        load_w(g_begin + 1 < g_end ? g_begin + 1 : g_begin, wx);
         {
-            constexpr int last = large_segments<RT>() - 1;
-            const int r0 = large_seg_first<RT>(last), cnt = large_seg_count<RT>(last);
-#pragma unroll
-            for (int c = 0; c < cnt; ++c)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    acc[r0 + c][v] = __builtin_fmaf(sc, Q[(r0 + c) & 1][v], acc[r0 + c][v]);
+            const uint32_t zz = (wy.z & 0xFu) * 0x01010101u;
+    #pragma unroll
+            for (int ks = 0; ks < 8; ++ks) B0[ks] = unpack8_bf16(wy.w[ks], zz);
+            sc0 = scale_of(wy);
         }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    load_a(g_begin, ar);
-    load_w(g_begin, wy);
-    load_w(g_begin + 1 < g_end ? g_begin + 1 : g_begin, wx);
-    {
-        const uint32_t zz = (wy.z & 0xFu) * 0x01010101u;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) B0[ks] = unpack8_bf16(wy.w[ks], zz);
-        sc0 = scale_of(wy);
-    }
-    store_a(0, ar);
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    for (int g = g_begin; g < g_end; g += 2) {
-        group_step(g, wx, wy, B0, B1, sc0, sc1);
-        if (g + 1 >= g_end) break;
-        group_step(g + 1, wy, wx, B1, B0, sc1, sc0);
-    }
-
-    // Lane holds column col and rows rt*32 + 8 (v / 4) + 4 h + v % 4 of the block.  Without
-    // a K split the results go to C; with one, each split writes its partial product to its
-    // own [M, N] slice and w4a16_split_reduce adds the slices in split order (the kernel
-    // boundary orders the two).
-    float *out = p.splits == 1 ? p.C : p.part + (int64_t)sp * p.stride;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t row = m0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (row < m_end && col < N) out[row * N + col] = acc[rt][v];
+        store_a(0, ar);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        for (int g = g_begin; g < g_end; g += 2) {
+            group_step(g, wx, wy, B0, B1, sc0, sc1);
+            if (g + 1 >= g_end) break;
+            group_step(g + 1, wy, wx, B1, B0, sc1, sc0);
         }
+
+        // Lane holds column col and rows rt*32 + 8 (v / 4) + 4 h + v % 4 of the block.  A
+        // segment of the whole tile writes C; any other writes its partial product to its slice
+        // of the [M, N] partials, and a second launch (w4a16_split_reduce where every tile is
+        // split alike, else w4a16_tile_reduce) adds each tile's slices in workgroup order (the
+        // kernel boundary orders the two).
+        float *out = g_begin == 0 && g_end == p.groups ? p.C : p.part + (int64_t)slot * p.stride;
+    #pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+    #pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int64_t row = m0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (row < m_end && col < N) out[row * N + col] = acc[rt][v];
+            }
+        // Wider row blocks never share tiles (the plan keeps them to whole-tile splits, which
+        // the host checks): their kernels hold one segment, with the register use and
+        // schedule of a kernel without the loop.
+        if constexpr (!kShared) break;
+        u += (uint32_t)(g_stop - g_begin);
+        if (u >= u_end) break;
+    }
 }
 
 // Sums the split-K partial products in split order: C[i] = sum_s part[s * stride + i],
@@ -1407,7 +1441,15 @@ __global__ __launch_bounds__(256) void w4a16_split_reduce(const float *__restric
     const int64_t n4 = total / 4;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
         f32x4 acc = *(const f32x4 *)(part + 4 * i);
-        for (int s2 = 1; s2 < splits; ++s2) acc += *(const f32x4 *)(part + (int64_t)s2 * stride + 4 * i);
+        if (splits >= 12) {
+            // deep splits: loads run ahead of the (ordered) additions (17 slices at M=40: 5.5 ->
+            // 4.4 us); with few slices the plain loop measured faster over a whole step (the
+            // next kernel starts later after the unrolled one: M=160 step +1%)
+#pragma unroll 4
+            for (int s2 = 1; s2 < splits; ++s2) acc += *(const f32x4 *)(part + (int64_t)s2 * stride + 4 * i);
+        } else {
+            for (int s2 = 1; s2 < splits; ++s2) acc += *(const f32x4 *)(part + (int64_t)s2 * stride + 4 * i);
+        }
         *(f32x4 *)(C + 4 * i) = acc;
     }
     if (blockIdx.x == 0 && threadIdx.x < total - 4 * n4) {
@@ -1415,6 +1457,48 @@ __global__ __launch_bounds__(256) void w4a16_split_reduce(const float *__restric
         float acc = part[e];
         for (int s2 = 1; s2 < splits; ++s2) acc += part[(int64_t)s2 * stride + e];
         C[e] = acc;
+    }
+}
+
+// Adds each output tile's partial products in workgroup order.  Tile t (row block
+// t / n_tiles, column tile t % n_tiles) owns the steps a = t * group_stride .. a + groups - 1
+// of the large-M kernel's numbering, so workgroups floor(a / gps) .. floor((a + groups - 1)
+// / gps) wrote its partials, to slices 0, 1, ... in that order:
+//   C[r, c] = part[0][r, c] + part[1][r, c] + ... (left to right).
+// Every tile has at least two slices here (the plan launches this only when no workgroup
+// holds a whole tile).  One thread per four columns of a row, rows blockIdx.y + i gridDim.y;
+// N % 4 == 0 takes 16-byte accesses (C and every slice are 16-byte aligned: stride % 4 == 0).
+// Step numbers stay below 2^31 (checked on the host).
+__global__ __launch_bounds__(256) void w4a16_tile_reduce(const float *__restrict__ part, float *__restrict__ C, int M,
+                                                         int N, int64_t stride, int block_rows, int n_tiles,
+                                                         int groups, int group_stride, int gps)
+{
+    const int c0 = ((int)blockIdx.x * 256 + (int)threadIdx.x) * 4;
+    if (c0 >= N) return;
+    // a wave's 256 columns are one column tile, so the tile arithmetic is scalar
+    const uint32_t nt = __builtin_amdgcn_readfirstlane((uint32_t)c0 / kLTileN);
+    for (int row = (int)blockIdx.y; row < M; row += (int)gridDim.y) {
+        const int64_t e = (int64_t)row * N + c0;
+        f32x4 v0 = {}, v1 = {};
+        if ((N & 3) == 0) {  // the two slices every tile has, loaded before the tile arithmetic
+            v0 = *(const f32x4 *)(part + e);
+            v1 = *(const f32x4 *)(part + stride + e);
+        }
+        const uint32_t t = (uint32_t)(row / block_rows) * (uint32_t)n_tiles + nt;
+        const uint32_t a = t * (uint32_t)group_stride;
+        const int nseg = (int)((a + (uint32_t)groups - 1) / (uint32_t)gps - a / (uint32_t)gps) + 1;
+        if ((N & 3) == 0) {
+            f32x4 acc = v0 + v1;
+#pragma unroll 4
+            for (int k = 2; k < nseg; ++k) acc += *(const f32x4 *)(part + k * stride + e);
+            *(f32x4 *)(C + e) = acc;
+        } else {
+            for (int j = 0; j < 4 && c0 + j < N; ++j) {
+                float acc = part[e + j];
+                for (int k = 1; k < nseg; ++k) acc += part[k * stride + e + j];
+                C[e + j] = acc;
+            }
+        }
     }
 }
 
@@ -1904,6 +1988,15 @@ constexpr double kLargeClockGHz = 2.4;
 constexpr double kLargeEff = 0.44;         // sustained fraction of the issue-limited rate (measured)
 constexpr double kUsLargeReduce = 2.5;     // second launch (split reduction) and its ramp
 constexpr double kLargeReduceGBs = 4000.0; // split reduction: partial reads + C writes
+// Evenly shared steps (a workgroup may end one tile and start the next): the second tile
+// costs another ramp and another partial write, 2.6 us at 40 rows (per-workgroup
+// timestamps: 1.3 us ramp, 1.3 us write).  They pay where whole-tile splits need extra
+// rounds of workgroups: Qwen2.5-7B gate_up at M=40, 5 splits in 3 rounds of 6 groups
+// against 17 shared steps in one round, 44.3 -> 37.5 us.  From three row tiles on they
+// measured slower than the splits (M=80 gate_up 47.4 -> 49.3 us, M=160 qkv 34.4 -> 41.5,
+// gate_up 50.7 -> 55.8): with more CUs busy each group's matrix-core work slows (M=160
+// gate_up: 2.45 us per group on 172 CUs, 2.79 on 251), and the partials grow with the rows.
+constexpr double kUsLargeSegment = 2.6;
 // Which kernel: from M = 64 on, every shape runs on the bf16 kernel (the small-M kernel
 // would dequantize each weight once per 16-row block).  From M = 17 (more than one 16-row
 // block) the bf16 kernel also wins on large GEMMs, where its one dequantization per weight
@@ -1932,21 +2025,36 @@ double large_group_us(int rt)
 // rt1_max_m rows.
 struct LargeChoice {
     double us;
-    int mb, splits, rows;
+    int mb, splits, rows, gps, stride;  // splits: most partial slices any tile receives
 };
+
+// Most partial slices any tile receives when tile t owns steps t * stride .. + groups - 1
+// and workgroup w takes steps w * gps .. + gps - 1.  t * stride mod gps repeats with a
+// period that divides gps, so the first min(tiles, gps) tiles show every case.
+int large_max_segments(int64_t tiles, int groups, int stride, int gps)
+{
+    int most = 1;
+    for (int64_t t = 0; t < tiles && t < gps; ++t) {
+        const int64_t a = t * stride;
+        const int n = (int)((a + groups - 1) / gps - a / gps) + 1;
+        most = n > most ? n : most;
+    }
+    return most;
+}
 
 LargeChoice search_large_plan(int64_t M, int64_t K, int64_t N, int min_gps, int64_t rt1_max_m)
 {
     const int groups = (int)(K / kGroup);
     const int n_tiles = (int)((N + kLTileN - 1) / kLTileN);
     const int min_blocks = (int)((M + kLMaxRT * 32 - 1) / (kLMaxRT * 32));
-    LargeChoice best = {1e30, min_blocks, 1, 0};
+    LargeChoice best = {1e30, min_blocks, 1, 0, groups, groups};
     for (int mbk = min_blocks; mbk <= 2 * min_blocks; ++mbk) {
         const int rows = (int)((M + mbk - 1) / mbk);
         const int rt = (rows + 31) / 32;
         if ((rt < 2 && M > rt1_max_m) || (int64_t)(mbk - 1) * rows >= M) continue;
         const int64_t base = (int64_t)mbk * n_tiles;
         const double tg = large_group_us(rt);
+        // tiles split alike: sp workgroups per tile (stride sp * gps)
         for (int sp = 1; sp <= groups; ++sp) {
             const int gps = (groups + sp - 1) / sp;
             if ((groups + gps - 1) / gps != sp) continue;
@@ -1954,7 +2062,19 @@ LargeChoice search_large_plan(int64_t M, int64_t K, int64_t N, int min_gps, int6
             const int64_t rounds = (base * sp + kCUs - 1) / kCUs;
             double us = (double)rounds * gps * tg;
             if (sp > 1) us += kUsLargeReduce + (double)(sp + 1) * M * N * 4 / (kLargeReduceGBs * 1e3);
-            if (us < best.us) best = {us, mbk, sp, rows};
+            if (us < best.us) best = {us, mbk, sp, rows, gps, sp * gps};
+        }
+        // the steps shared out evenly (stride = groups): only where gps does not divide the
+        // groups (otherwise the same as a split above), and only for blocks of up to two row
+        // tiles (see kLargeSharedMaxRT)
+        for (int gps = min_gps > 1 ? min_gps : 1; gps < groups && rt <= kLargeSharedMaxRT; ++gps) {
+            if (groups % gps == 0) continue;
+            const int64_t wgs = (base * groups + gps - 1) / gps;
+            const int64_t rounds = (wgs + kCUs - 1) / kCUs;
+            const double slices = (double)(wgs + base - 1) / (double)base;  // mean per tile
+            const double us = (double)rounds * gps * tg + kUsLargeSegment + kUsLargeReduce +
+                              (slices + 1) * M * N * 4 / (kLargeReduceGBs * 1e3);
+            if (us < best.us) best = {us, mbk, large_max_segments(base, groups, groups, gps), rows, gps, groups};
         }
     }
     return best;
@@ -1962,7 +2082,6 @@ LargeChoice search_large_plan(int64_t M, int64_t K, int64_t N, int min_gps, int6
 
 void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
 {
-    const int groups = (int)(K / kGroup);
     const int n_tiles = (int)((N + kLTileN - 1) / kLTileN);
     // First choice: splits of at least 4 groups, and one-tile row blocks up to 64 rows.
     // With fewer groups per workgroup its ramp and the partial tile it writes at the end
@@ -1970,21 +2089,22 @@ void make_large_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     // projections at M = 64..96 ran 19-22% faster with 2 row blocks x 7 splits than with
     // the 1 x 14 the model alone picks (M=64 qkv: 19.5 -> 15.7 us).  The model's choice
     // stands where that plan would leave more than half of the CUs idle.
+    auto workgroups = [&](const LargeChoice &c) {
+        return ((int64_t)c.mb * n_tiles * c.stride + c.gps - 1) / c.gps;
+    };
     LargeChoice c = search_large_plan(M, K, N, 4, 64);
-    if ((int64_t)c.mb * n_tiles * c.splits < kCUs / 2) c = search_large_plan(M, K, N, 1, 32);
-    const int best_mb = c.mb, best_s = c.splits, best_rows = c.rows;
-    const int gps = (groups + best_s - 1) / best_s;
-    const int64_t base = (int64_t)best_mb * n_tiles;
+    if (workgroups(c) < kCUs / 2) c = search_large_plan(M, K, N, 1, 32);
     pl->kernel = 3;
-    pl->tile_m = best_rows;
+    pl->tile_m = c.rows;
     pl->tile_n = kLTileN;
-    pl->m_blocks = best_mb;
+    pl->m_blocks = c.mb;
     pl->n_tiles = n_tiles;
-    pl->splits = best_s;
-    pl->groups_per_split = gps;
+    pl->splits = c.splits;
+    pl->groups_per_split = c.gps;
     pl->full_tiles = 0;
-    pl->workgroups = base * best_s;
-    pl->workspace_bytes = best_s > 1 ? best_s * ((M * N + 3) / 4 * 4) * 4 : 0;
+    pl->workgroups = workgroups(c);
+    pl->workspace_bytes = c.splits > 1 ? c.splits * ((M * N + 3) / 4 * 4) * 4 : 0;
+    pl->group_stride = c.stride;
 }
 
 // Kernel ids of the small-M shapes: 1 / 2 (4-bit codes, wide / tall), 4 / 5 (8-bit codes),
@@ -2074,6 +2194,7 @@ void make_small_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl, int bits = 4,
     pl->splits = splits;
     pl->groups_per_split = gps;
     pl->full_tiles = (int)full;
+    pl->group_stride = 0;
     pl->workgroups = full + (base - full) * splits;
     pl->workspace_bytes = split_tiles * 4 + split_tiles * splits * rows * kTileN * 4;
 }
@@ -2104,6 +2225,7 @@ void make_narrow_plan(int64_t M, int64_t K, int64_t N, w4_plan *pl)
     pl->splits = 1;
     pl->groups_per_split = (int)(K / kGroup);
     pl->full_tiles = 0;
+    pl->group_stride = 0;
     pl->workgroups = pl->n_tiles;
     pl->workspace_bytes = 0;
 }
@@ -2306,14 +2428,24 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         q.n_tiles = pl.n_tiles;
         q.m_blocks = pl.m_blocks;
         q.block_rows = pl.tile_m;
-        if (q.n_tiles != (N + kLTileN - 1) / kLTileN) {  // the kernel derives the tile count from N
-            set_error("%s: internal error: plan tiles (%d) do not follow from N", name, q.n_tiles);
+        const int64_t gstride = pl.group_stride;
+        // The kernel derives the tile and row-block counts from N, M and the block rows, and
+        // numbers the (tile, group) steps in 32 bits; the reduction relies on every tile
+        // having two or more workgroups whenever it runs.
+        const int64_t steps = (int64_t)q.m_blocks * q.n_tiles * gstride;
+        if (q.n_tiles != (N + kLTileN - 1) / kLTileN || q.m_blocks != (M + q.block_rows - 1) / q.block_rows ||
+            gstride < q.groups || q.gps < 1 || steps + q.gps >= ((int64_t)1 << 31) ||
+            pl.workgroups != (steps + q.gps - 1) / q.gps ||
+            (pl.splits > 1) != (q.gps < q.groups) ||
+            (gstride != (int64_t)pl.splits * q.gps && (q.block_rows + 31) / 32 > kLargeSharedMaxRT) ||
+            pl.splits != large_max_segments((int64_t)q.m_blocks * q.n_tiles, q.groups, (int)gstride, q.gps)) {
+            set_error("%s: internal error: inconsistent large-M plan", name);
             return W4_ERR_PLAN;
         }
         const LargeTail tail = {q.C, q.part, q.stride};
 #define W4_LAUNCH_L(RTV)                                                                                          \
     hipLaunchKernelGGL((w4a16_mfma_kernel<RTV>), grid, dim3(kLThreads), 0, s, q.A, q.Wq, q.S, q.Z, (int)q.M, (int)q.K, \
-                       (int)q.N, q.gps, q.splits, q.block_rows, tail)
+                       (int)q.N, q.gps, (int)gstride, q.block_rows, tail)
         switch ((pl.tile_m + 31) / 32) {
         case 1: W4_LAUNCH_L(1); break;
         case 2: W4_LAUNCH_L(2); break;
@@ -2325,11 +2457,17 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
         if (pl.splits > 1) {
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return hip_fail(name, e);
-            const int64_t n4 = M * N / 4;
-            int64_t blocks = (n4 + 255) / 256;
-            blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
-            hipLaunchKernelGGL(w4a16_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, C, M * N, q.stride,
-                               pl.splits);
+            if (gstride == (int64_t)pl.splits * q.gps) {  // every tile split alike
+                const int64_t n4 = M * N / 4;
+                int64_t blocks = (n4 + 255) / 256;
+                blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+                hipLaunchKernelGGL(w4a16_split_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, C, M * N,
+                                   q.stride, pl.splits);
+            } else {
+                const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)(M < 65535 ? M : 65535));
+                hipLaunchKernelGGL(w4a16_tile_reduce, rgrid, dim3(256), 0, s, part, C, (int)M, (int)N, q.stride,
+                                   q.block_rows, q.n_tiles, q.groups, (int)gstride, q.gps);
+            }
         }
     } else {
         SmallParams p;

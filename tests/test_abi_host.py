@@ -213,14 +213,28 @@ def test_plan_covers_shapes():
                 assert (p["tile_m"], p["tile_n"]) == ((32 if a4 and 16 < M <= 32 else 16), 64)
             assert p["n_tiles"] * p["tile_n"] >= N > (p["n_tiles"] - 1) * p["tile_n"]
             assert p["m_blocks"] * p["tile_m"] >= M > (p["m_blocks"] - 1) * p["tile_m"]
-            assert p["splits"] * p["groups_per_split"] >= groups
-            assert (p["splits"] - 1) * p["groups_per_split"] < groups
             tiles = p["n_tiles"] * p["m_blocks"]
             full = p["full_tiles"]
             assert full % 256 == 0 and 0 <= full < tiles
             assert full == 0 or (p["kernel"] in (1, 4, 6) and p["splits"] > 1)
-            assert p["workgroups"] == full + (tiles - full) * p["splits"]
             assert (p["workspace_bytes"] > 0) == (p["splits"] > 1)
+            gps, stride = p["groups_per_split"], p["group_stride"]
+            if p["kernel"] == 3 and stride == groups and groups % gps:
+                # steps shared out evenly: walk every workgroup's range and count the
+                # workgroups each tile receives
+                assert 1 <= gps < groups and p["tile_m"] <= 64  # blocks of up to two row tiles
+                assert p["workgroups"] == -(-tiles * groups // gps)
+                per_tile = [0] * tiles
+                for w in range(p["workgroups"]):
+                    u, end = w * gps, min(w * gps + gps, tiles * groups)
+                    for t in range(u // groups, (end - 1) // groups + 1):
+                        per_tile[t] += 1
+                assert p["splits"] == max(per_tile) and min(per_tile) >= 2
+            else:  # each tile split alike into `splits` workgroups (kernel 3: stride = their span)
+                assert stride == (p["splits"] * gps if p["kernel"] == 3 else 0)
+                assert p["splits"] * gps >= groups
+                assert (p["splits"] - 1) * gps < groups
+                assert p["workgroups"] == full + (tiles - full) * p["splits"]
             if p["kernel"] not in (3, 8):  # every workgroup resident at once
                 per_cu = (2 if p["tile_m"] == 32 else 3) if p["kernel"] in (1, 4, 6) else 1
                 assert p["workgroups"] <= 256 * per_cu or p["splits"] == 1
@@ -277,6 +291,15 @@ def test_measured_plan_choices():
                           (160, 11008, 4096, (1, 160, 15))):
         p = w4.plan(M, K, N)
         assert p["kernel"] == 3 and (p["m_blocks"], p["tile_m"], p["splits"]) == want, (M, K, N, p)
+    # bf16 kernel at M = 17..64 on wide outputs: the (tile, group) steps shared out evenly,
+    # one round of workgroups instead of 2-3 rounds of whole-tile splits (Qwen2.5-7B gate_up
+    # at M=40: 5 splits in 3 rounds 45.8 us, 17 shared steps 38.3 us; M=24 36.9 -> 32.4;
+    # Llama-2-7B gate_up at M=24: 31.2 -> 25.0)
+    for M, K, N, want in ((40, 3584, 37888, (17, 244, 3)), (24, 3584, 37888, (17, 244, 3)),
+                          (24, 4096, 22016, (11, 251, 4))):
+        p = w4.plan(M, K, N)
+        assert p["kernel"] == 3 and p["group_stride"] == K // 128, (M, K, N, p)
+        assert (p["groups_per_split"], p["workgroups"], p["splits"]) == want, (M, K, N, p)
     # a single 16-row block hands a tall plan at one group per wave to the wide shape (M=1
     # draft: qkv 4.52 -> 4.49, o 4.70 -> 4.57, down 7.36 -> 7.16 us; 8-bit qkv 5.69 -> 5.36 us);
     # more rows per workgroup keep the tall shape (W4A4 at M=32: 9.21 tall, 10.30 wide)

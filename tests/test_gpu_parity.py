@@ -220,6 +220,30 @@ def test_mid_m_bf16_path(orc, M, K, N):
     check(C[:, cols], Cr, Cabs, f"mid-M M={M} K={K} N={N}")
 
 
+@pytest.mark.parametrize("M,K,N,full", [(17, 1664, 33333, True), (17, 2048, 40003, True), (23, 1792, 33333, True),
+                                        (40, 2688, 24576, True), (48, 3584, 37888, False), (64, 3584, 37888, False)])
+def test_shared_steps(orc, M, K, N, full):
+    # plans whose (tile, group) steps are shared out evenly: workgroups that end one tile and
+    # start the next, tiles with 3-4 partial slices, the per-tile reduction (scalar path for
+    # N % 4 != 0), one and two row tiles; every element, or the columns around the tile
+    # edges plus a random sample
+    p = w4.plan(M, K, N)
+    log(f"shared steps M={M} K={K} N={N} plan={p}")
+    G = K // 128
+    assert p["kernel"] == 3 and p["group_stride"] == G and G % p["groups_per_split"] and p["splits"] >= 3
+    x = synth.generate_custom(M, K, N, seed=43)
+    out = torch.full((M, N), float("nan"), device="cuda")
+    C = run(to_dev(x), out=out).cpu().numpy()
+    if full:
+        Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z)
+    else:
+        edges = np.arange(256, N, 256)
+        cols = np.unique(np.r_[0, N - 1, edges - 1, edges, np.random.default_rng(44).integers(0, N, 64)])
+        Cr, Cabs = orc.gemm(x.A, x.Wq, x.S, x.Z, cols=cols)
+        C = C[:, cols]
+    check(C, Cr, Cabs, f"shared steps M={M} K={K} N={N}")
+
+
 @pytest.mark.parametrize("M,K,N", [(5, 65536, 65528), (64, 65536, 65528), (63, 1 << 24, 1), (8191, 131072, 8)])
 def test_maximum_sizes(orc, M, K, N):
     # the largest arrays the kernels' 32-bit byte offsets address: packed weights
@@ -707,7 +731,8 @@ def test_large_m_unaligned_scale_view(orc):
 
 
 def test_large_m_graph_and_reproducible():
-    shapes = [(160, 4096, 4096), (160, 4096, 22016), (160, 11008, 4096)]
+    # (the last two shapes share their (tile, group) steps out evenly)
+    shapes = [(160, 4096, 4096), (160, 4096, 22016), (160, 11008, 4096), (40, 3584, 37888), (17, 2048, 40003)]
     xs = [to_dev(synth.generate_custom(M, K, N, seed=29)) for (M, K, N) in shapes]
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):

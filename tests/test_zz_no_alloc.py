@@ -24,9 +24,11 @@ def _alloc(dev, out, stream):
 
 
 # two calls in a row on each path, the second smaller: small-M split plans (tall and wide,
-# balanced), an unsplit plan, and the bf16 kernel's split slices
+# balanced), an unsplit plan, the bf16 kernel's split slices, and its (tile, group) steps
+# shared out evenly
 CASES = [((5, 18944, 3584), (3, 3584, 4608)), ((5, 3584, 37888), (1, 1536, 17920)),
-         ((160, 4096, 12288), (64, 3584, 3584)), ((7, 1536, 1536), (2, 256, 96))]
+         ((160, 4096, 12288), (64, 3584, 3584)), ((7, 1536, 1536), (2, 256, 96)),
+         ((40, 3584, 37888), (17, 2048, 40003))]
 
 
 @pytest.mark.parametrize("first,second", CASES, ids=lambda c: "x".join(map(str, c)))
@@ -80,7 +82,7 @@ def test_noalloc_captures_a_new_split_shape_without_warm_up():
 def test_noalloc_rejects_a_plan_beyond_its_scratch():
     # a plan whose split slices (M*N*splits*4 bytes) exceed the 64 MiB scratch: a clear error
     # before anything is launched, and C is left as it was (real buffers of the right sizes)
-    M, K, N = 320, 8192, 11008
+    M, K, N = 1312, 6144, 7680  # 3 slices of M*N floats: 115 MiB
     p = w4.plan(M, K, N)
     log(f"noalloc oversize plan={p}")
     assert p["workspace_bytes"] > (64 << 20) - (256 << 10)
