@@ -1256,7 +1256,7 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
         // of the group; rows outside the block read row m_end - 1 (never stored).
         uint32_t aoff[kAChunks];
         int alds[kAChunks];
-    #pragma unroll
+#pragma unroll
         for (int j = 0; j < kAChunks; ++j) {
             const int id = (int)tid + kLThreads * j;
             const int row = id >> 4, kc = id & 15;
@@ -1265,15 +1265,15 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
             alds[j] = row * kARowBytes + kc * 16;
         }
         auto load_a = [&](int g, u32x4 (&ar)[kAChunks]) {
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < kAChunks; ++j) ar[j] = __builtin_amdgcn_raw_buffer_load_b128(rs.A, aoff[j], (uint32_t)g * (kGroup * 2), 0);
         };
         auto store_a = [&](int buf, const u32x4 (&ar)[kAChunks]) {
-    #pragma unroll
+#pragma unroll
             for (int j = 0; j < kAChunks; ++j) *(u32x4 *)(lds + buf * kBuf + alds[j]) = ar[j];
         };
         auto load_w = [&](int g, LargeW &r) {
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < 8; ++ks)
                 r.w[ks] = __builtin_amdgcn_raw_buffer_load_b32(rs.W, woff, ((uint32_t)g * 16 + 2 * ks) * rowbytes, kCacheStream);
             r.s = __builtin_amdgcn_raw_buffer_load_b16(rs.S, soff, (uint32_t)g * (uint32_t)N * 2, 0);
@@ -1282,9 +1282,9 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
         auto scale_of = [](const LargeW &r) { return (float)__builtin_bit_cast(_Float16, (uint16_t)r.s); };
 
         f32x16 acc[RT];
-    #pragma unroll
+#pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-    #pragma unroll
+#pragma unroll
             for (int v = 0; v < 16; ++v) acc[rt][v] = 0.f;
 
         // A operand of (row tile rt, k-step ks): row rt*32 + c, k = 16 ks + 8 h .. + 7
@@ -1310,7 +1310,7 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
             __builtin_amdgcn_sched_barrier(0);
             // Pin this group's dequantization inside this group: without it the compiler may
             // hoist it into the previous group, where it would wait for loads just issued.
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Wn.w[ks]));
             asm volatile("" : "+v"(Wn.z), "+v"(Wn.s));
 
@@ -1321,7 +1321,7 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
             auto a_at = [&](int n) {
                 return *(const bf16x8 *)(abase + large_step_rt<RT>(n) * 32 * kARowBytes + large_step_ks<RT>(n) * 32);
             };
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < kAhead; ++i) ring[i] = a_at(i);
             // MFMA step n runs (row tile, k-step) = (large_step_rt, large_step_ks): the row tiles
             // go in segments of one or two, and a segment of two interleaves its tiles' chains
@@ -1332,13 +1332,13 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
             // order.  Row tile rt accumulates in chain rt % 2 and is rescaled from Q[rt % 2].
             Unpack8 u;
             f32x16 P[2], Q[2];
-    #pragma unroll
+#pragma unroll
             for (int sg = 0; sg < large_segments<RT>(); ++sg) {
                 const int r0 = large_seg_first<RT>(sg), cnt = large_seg_count<RT>(sg);
                 const int base = 8 * r0, len = 8 * cnt;
                 const int pr0 = sg > 0 ? large_seg_first<RT>(sg - 1) : 0;
                 const int pending = sg > 0 ? 16 * large_seg_count<RT>(sg - 1) : 0;
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < len; ++i) {
                     const int n = base + i;
                     const int rt = large_step_rt<RT>(n), ks = large_step_ks<RT>(n);
@@ -1352,13 +1352,13 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
                         Pc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, Bc[ks], Pc, 0, 0, 0);
                     }
                     const int word = n / RT, l = n % RT;
-    #pragma unroll
+#pragma unroll
                     for (int pc = l * 5 / RT; pc < (l + 1) * 5 / RT; ++pc) unpack8_piece(pc, u, Wn.w[word], zzn);
                     if (l == RT - 1) Bn[word] = __builtin_bit_cast(bf16x8, u.r);
                     // the previous segment's partials, spread over steps 1 .. len - 1
                     if (pending > 0 && i > 0) {
                         const int f0 = (i - 1) * pending / (len - 1), f1 = i * pending / (len - 1);
-    #pragma unroll
+#pragma unroll
                         for (int f = f0; f < f1; ++f) {
                             const int tr = pr0 + f / 16, v = f % 16;
                             acc[tr][v] = __builtin_fmaf(sc, Q[tr & 1][v], acc[tr][v]);
@@ -1366,7 +1366,7 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
-    #pragma unroll
+#pragma unroll
                 for (int c = 0; c < cnt; ++c) {
                     Q[(r0 + c) & 1] = P[(r0 + c) & 1];
                     // stage one chunk of the next group's activations per row tile, so the LDS
@@ -1376,7 +1376,7 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
             }
             scn = scale_of(Wn);
             // ... and keep it from sinking into the next group: the operands are complete here.
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(Bn[ks]));
             // The barrier comes as soon as this wave's LDS traffic for the group is done; the
             // last row tile's rescale (which waits for its MFMAs) follows it.
@@ -1384,9 +1384,9 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
             {
                 constexpr int last = large_segments<RT>() - 1;
                 const int r0 = large_seg_first<RT>(last), cnt = large_seg_count<RT>(last);
-    #pragma unroll
+#pragma unroll
                 for (int c = 0; c < cnt; ++c)
-    #pragma unroll
+#pragma unroll
                     for (int v = 0; v < 16; ++v)
                         acc[r0 + c][v] = __builtin_fmaf(sc, Q[(r0 + c) & 1][v], acc[r0 + c][v]);
             }
@@ -1398,7 +1398,7 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
         load_w(g_begin + 1 < g_end ? g_begin + 1 : g_begin, wx);
         {
             const uint32_t zz = (wy.z & 0xFu) * 0x01010101u;
-    #pragma unroll
+#pragma unroll
             for (int ks = 0; ks < 8; ++ks) B0[ks] = unpack8_bf16(wy.w[ks], zz);
             sc0 = scale_of(wy);
         }
@@ -1416,9 +1416,9 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
         // split alike, else w4a16_tile_reduce) adds each tile's slices in workgroup order (the
         // kernel boundary orders the two).
         float *out = g_begin == 0 && g_end == p.groups ? p.C : p.part + (int64_t)slot * p.stride;
-    #pragma unroll
+#pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-    #pragma unroll
+#pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t row = m0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (row < m_end && col < N) out[row * N + col] = acc[rt][v];
