@@ -1172,11 +1172,15 @@ struct LargeW {
     uint32_t z;   // zero byte
 };
 
-template <int RT>
+// SH: plans with shared steps (a workgroup may hold two tiles' steps; blocks of up to
+// kLargeSharedMaxRT row tiles).  Without it a workgroup holds one segment, and the kernel has
+// the register use and schedule of one without the segment loop.
+template <int RT, bool SH>
 __global__ __launch_bounds__(kLThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S, const uint8_t *Z, int M_, int K_,
                        int N_, int groups_per_split, int group_stride, int block_rows, LargeTail tail)
 {
+    static_assert(!SH || RT <= kLargeSharedMaxRT, "shared steps: blocks of up to two row tiles");
     constexpr int kRows = RT * 32;
     constexpr int kBuf = kRows * kARowBytes;
     constexpr int kAChunks = kRows * kChunksPerRow / kLThreads;  // == RT: one per row tile
@@ -1198,7 +1202,7 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
     p.splits = 0;  // not used by the kernel
     p.gps = groups_per_split;
     p.n_tiles = (N_ + kLTileN - 1) / kLTileN;
-    p.m_blocks = RT <= kLargeSharedMaxRT ? (M_ + block_rows - 1) / block_rows : 0;  // (not needed otherwise)
+    p.m_blocks = SH ? (M_ + block_rows - 1) / block_rows : 0;  // (not needed otherwise)
     p.block_rows = block_rows;
 
     const int64_t N = p.N;
@@ -1219,10 +1223,10 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
     // piece of a tile (a segment) is accumulated on its own; a segment covering the whole
     // tile goes to C, any other to the partial-product slice numbered by the workgroup's
     // place among the tile's workgroups (w - floor(t * group_stride / groups_per_split)).
-    // Wider row blocks only ever take whole-tile splits (group_stride = splits * gps, checked
-    // on the host): a workgroup's steps lie in one tile, so neither the step count nor the
-    // end of the range is needed (one division less on the way to the first loads).
-    constexpr bool kShared = RT <= kLargeSharedMaxRT;
+    // Without shared steps (group_stride = splits * gps, checked on the host) a workgroup's
+    // steps lie in one tile, so neither the step count nor the end of the range is needed
+    // (one division less on the way to the first loads).
+    constexpr bool kShared = SH;
     const uint32_t total = kShared ? (uint32_t)p.m_blocks * (uint32_t)p.n_tiles * (uint32_t)group_stride : 0u;
     uint32_t u = blockIdx.x * (uint32_t)p.gps;
     const uint32_t u_end = u + (uint32_t)p.gps < total ? u + (uint32_t)p.gps : total;
@@ -1423,9 +1427,7 @@ void w4a16_mfma_kernel(const uint16_t *A, const uint32_t *Wq, const uint16_t *S,
                 const int64_t row = m0 + rt * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
                 if (row < m_end && col < N) out[row * N + col] = acc[rt][v];
             }
-        // Wider row blocks never share tiles (the plan keeps them to whole-tile splits, which
-        // the host checks): their kernels hold one segment, with the register use and
-        // schedule of a kernel without the loop.
+        // without shared steps the workgroup holds one segment
         if constexpr (!kShared) break;
         u += (uint32_t)(g_stop - g_begin);
         if (u >= u_end) break;
@@ -2443,15 +2445,16 @@ w4_status run_gemm(int bits, bool a4, const char *name, const void *A_bf16, cons
             return W4_ERR_PLAN;
         }
         const LargeTail tail = {q.C, q.part, q.stride};
-#define W4_LAUNCH_L(RTV)                                                                                          \
-    hipLaunchKernelGGL((w4a16_mfma_kernel<RTV>), grid, dim3(kLThreads), 0, s, q.A, q.Wq, q.S, q.Z, (int)q.M, (int)q.K, \
-                       (int)q.N, q.gps, (int)gstride, q.block_rows, tail)
+#define W4_LAUNCH_L(RTV, SHV)                                                                                     \
+    hipLaunchKernelGGL((w4a16_mfma_kernel<RTV, SHV>), grid, dim3(kLThreads), 0, s, q.A, q.Wq, q.S, q.Z, (int)q.M,      \
+                       (int)q.K, (int)q.N, q.gps, (int)gstride, q.block_rows, tail)
+        const bool shared = gstride != (int64_t)pl.splits * q.gps;  // (then 1 or 2 row tiles, checked above)
         switch ((pl.tile_m + 31) / 32) {
-        case 1: W4_LAUNCH_L(1); break;
-        case 2: W4_LAUNCH_L(2); break;
-        case 3: W4_LAUNCH_L(3); break;
-        case 4: W4_LAUNCH_L(4); break;
-        default: W4_LAUNCH_L(5); break;
+        case 1: if (shared) { W4_LAUNCH_L(1, true); } else { W4_LAUNCH_L(1, false); } break;
+        case 2: if (shared) { W4_LAUNCH_L(2, true); } else { W4_LAUNCH_L(2, false); } break;
+        case 3: W4_LAUNCH_L(3, false); break;
+        case 4: W4_LAUNCH_L(4, false); break;
+        default: W4_LAUNCH_L(5, false); break;
         }
 #undef W4_LAUNCH_L
         if (pl.splits > 1) {
