@@ -1458,15 +1458,11 @@ __global__ __launch_bounds__(256) void w4a16_split_reduce(const float *__restric
     const int64_t n4 = total / 4;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
         f32x4 acc = __builtin_nontemporal_load((const f32x4 *)(part + 4 * i));
-        if (splits >= 12) {
-            // deep splits: loads run ahead of the (ordered) additions (17 slices at M=40: 5.5 ->
-            // 4.4 us); with few slices the plain loop measured faster over a whole step (the
-            // next kernel starts later after the unrolled one: M=160 step +1%)
+        // unrolled so that the loads run ahead of the (ordered) additions: 17 slices at M=40
+        // 5.5 -> 4.4 us; with the non-temporal loads also for few slices (M=80 step 2.957 ->
+        // 2.890 ms, M=160 4.248 -> 4.227)
 #pragma unroll 4
-            for (int s2 = 1; s2 < splits; ++s2) acc += __builtin_nontemporal_load((const f32x4 *)(part + (int64_t)s2 * stride + 4 * i));
-        } else {
-            for (int s2 = 1; s2 < splits; ++s2) acc += __builtin_nontemporal_load((const f32x4 *)(part + (int64_t)s2 * stride + 4 * i));
-        }
+        for (int s2 = 1; s2 < splits; ++s2) acc += __builtin_nontemporal_load((const f32x4 *)(part + (int64_t)s2 * stride + 4 * i));
         *(f32x4 *)(C + 4 * i) = acc;
     }
     if (blockIdx.x == 0 && threadIdx.x < total - 4 * n4) {
